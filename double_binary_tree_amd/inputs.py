@@ -1,0 +1,120 @@
+"""Seeded synthetic inputs and the named workloads.
+
+This module holds no reduction arithmetic: it only draws per-rank input
+arrays (numpy ``PCG64``; per-rank streams from ``SeedSequence.spawn``) and
+describes the workload shapes.  Both the oracle tests and the GPU path take
+their inputs from here.
+
+The workloads mirror the message-size sweeps of the pages' measurements
+(nccl-tests ``all_reduce_perf``: power-of-two per-rank sizes, sum, out-of-place
+and in-place), with the rank counts, node counts, channel counts, element
+types and value distributions fixed for this build.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+SEED_BASE = 20261202
+
+_STORAGE = {"i32": np.int32, "i64": np.int64, "f32": np.float32,
+            "f16": np.float16, "bf16": np.uint16}
+_ITEMSIZE = {"i32": 4, "i64": 8, "f32": 4, "f16": 2, "bf16": 2}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed_index: int          # seed = SEED_BASE + seed_index
+    nranks: int
+    nnodes: int
+    algos: tuple             # ("ring",), ("tree",) or both
+    nchannels: int
+    chunk_bytes: int
+    dtype: str
+    op: str
+    count: int               # elements per rank
+    dist: tuple              # ("int", lo, hi) | ("normal", sigma) | ("uniform", lo, hi)
+
+    @property
+    def itemsize(self) -> int:
+        return _ITEMSIZE[self.dtype]
+
+    @property
+    def bytes_per_rank(self) -> int:
+        return self.count * self.itemsize
+
+    def with_count(self, count: int) -> "Workload":
+        return replace(self, count=count)
+
+
+KiB = 1024
+MiB = 1024 * 1024
+
+WORKLOADS = {
+    # 4 ranks, one node, ring, one channel: the 4-rank step table shape.
+    "ring4_i32": Workload("ring4_i32", 1, 4, 1, ("ring",), 1, 512 * KiB, "i32", "sum",
+                          1024, ("int", -1000, 1000)),
+    # 8 ranks on one node (the tree is the intra-node chain), 12 channels.
+    "chain8_f32": Workload("chain8_f32", 2, 8, 1, ("ring", "tree"), 12, 512 * KiB, "f32", "sum",
+                           16 * MiB, ("normal", 1.0)),
+    # Double binary tree over 16 single-rank nodes (even: mirror).
+    "dtree16_bf16": Workload("dtree16_bf16", 3, 16, 16, ("tree",), 8, 512 * KiB, "bf16", "sum",
+                             16 * MiB, ("normal", 1.0)),
+    # Double binary tree over 15 single-rank nodes (odd: shift).
+    "dtree15_bf16": Workload("dtree15_bf16", 3, 15, 15, ("tree",), 8, 512 * KiB, "bf16", "sum",
+                             16 * MiB, ("normal", 1.0)),
+    # Ring vs tree sweep shape (count and channels vary per point).
+    "sweep8_f32": Workload("sweep8_f32", 4, 8, 1, ("ring", "tree"), 12, 512 * KiB, "f32", "sum",
+                           1 << 20, ("uniform", -1.0, 1.0)),
+    # Hierarchical: 4 nodes x 8 local ranks, chain inside, double tree across.
+    "hier4x8_f16": Workload("hier4x8_f16", 5, 32, 4, ("tree",), 16, 512 * KiB, "f16", "sum",
+                            8 * MiB, ("normal", 0.1)),
+    "hier4x8_i64": Workload("hier4x8_i64", 5, 32, 4, ("tree",), 16, 512 * KiB, "i64", "sum",
+                            8 * MiB, ("int", -(1 << 40), 1 << 40)),
+    "hier4x8_f32max": Workload("hier4x8_f32max", 5, 32, 4, ("tree",), 16, 512 * KiB, "f32", "max",
+                               8 * MiB, ("normal", 1.0)),
+}
+
+SWEEP_CHANNELS = (1, 4, 12, 32)
+SWEEP_COUNTS = tuple(1 << p for p in range(1, 27))   # 8 B .. 256 MiB of f32
+
+
+def _round_f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Input preparation only: round drawn float32 values to bf16 with torch's
+    CPU conversion (round to nearest even) and return the bit patterns."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def draw(rng: np.random.Generator, dtype: str, dist: tuple, count: int) -> np.ndarray:
+    kind = dist[0]
+    if kind == "int":
+        lo, hi = dist[1], dist[2]
+        return rng.integers(lo, hi, size=count, endpoint=True, dtype=np.int64).astype(_STORAGE[dtype])
+    if kind == "normal":
+        x = rng.standard_normal(count, dtype=np.float32) * np.float32(dist[1])
+    elif kind == "uniform":
+        x = rng.uniform(dist[1], dist[2], size=count).astype(np.float32)
+    else:
+        raise ValueError(f"unknown distribution {dist}")
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16)
+    if dtype == "bf16":
+        return _round_f32_to_bf16_bits(x)
+    raise ValueError(f"float distribution for integer dtype {dtype}")
+
+
+def rank_inputs(w: Workload, count: int | None = None, salt: int = 0) -> list[np.ndarray]:
+    """One input array per rank for workload ``w`` (optionally resized).
+
+    ``salt`` picks an independent stream family (used for extra test cases)."""
+    n = w.count if count is None else count
+    seed = SEED_BASE + w.seed_index + 1000 * salt
+    children = np.random.SeedSequence(seed).spawn(w.nranks)
+    return [draw(np.random.Generator(np.random.PCG64(ch)), w.dtype, w.dist, n) for ch in children]

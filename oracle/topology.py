@@ -1,0 +1,280 @@
+"""Oracle: tree topology of the all-reduce data path (test infrastructure only).
+
+Sources (page title, then section):
+
+* "NCCL 专家课程 13：Tree、双树、层次化连接与真实交叉区间" (blog.cptz.space, NCCL
+  course chapter 13), sections
+  - "先固定方向" and "数据结构不是纯二叉树": a tree record per channel holds a
+    parent (``up``, -1 at the root) and three child slots (``down``, -1 when
+    empty); the root has at most two children, any other rank at most three.
+  - "Btree 的 bit 构造": the node-level binary tree built from bit operations.
+  - "双树：偶数 mirror，奇数 shift": the second tree, mirrored for an even node
+    count and shifted by one for an odd node count.
+  - "节点内先形成链": inside a node the ranks form a chain (parent = previous
+    rank, first child = next rank) and the channel records are duplicated
+    so that each copy can carry one of the two node-level trees.
+  - "节点间连接": node-level edges are attached to each node's head rank; the
+    ``depth`` field is the approximation  L - 1 + floor(log2(nnodes)).
+  - "从 GRAPH 日志复原 active tree": the structural assertions (parent/child
+    symmetry, one root, N-1 edges, no cycle, every rank reaches the root).
+  - "直接执行源码中的 DTree": the probe table of roots and depths.
+
+Readings where the pages are silent (each listed in the design doc):
+
+* The intra-node order is the identity (local i = rank node*L + i) for every
+  channel; the head pattern is the plain tree pattern, so the parent head and
+  both child heads are local index 0.
+* Attaching a parent writes ``up``; attaching a child writes the first empty
+  ``down`` slot, children taken in the order child0 then child1; a full record
+  is an error.
+* Of ``nchannels`` channels the first ceil(nchannels/2) use tree 0 and the
+  rest tree 1 (the duplicated copies).  With one node both trees are the
+  bare chain.
+
+Pins (tests/test_oracle_topology.py): the probe table, the 4-node drawings,
+the chain roles, the structural assertions for every shape up to 64 ranks and
+the depth formula values that the pages work out.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+def btree(n: int, r: int) -> tuple[int, int, int, int | None]:
+    """Node-level binary tree over node indices 0..n-1.
+
+    Returns ``(parent, child0, child1, child_type)``.  Node 0 is the root and
+    has only the second child.  For r > 0, with b the lowest set bit of r, the
+    preferred parent clears b and sets the next higher bit; if that index does
+    not exist the parent only clears b.  The children sit b/2 below and b/2
+    above r; the upper child shrinks its offset by halves until it names an
+    existing node.  ``child_type`` says whether r lies below (0) or above (1)
+    its parent.  (Section "Btree 的 bit 构造".)
+    """
+    if not (0 <= r < n):
+        raise ValueError(f"rank {r} outside 0..{n - 1}")
+    bit = 1
+    while bit < n and not (bit & r):
+        bit <<= 1
+    if r == 0:
+        # The scan found no set bit: bit is now the smallest power of two >= n.
+        return -1, -1, (bit >> 1) if n > 1 else -1, None
+    parent = (r ^ bit) | (bit << 1)
+    if parent >= n:
+        parent = r ^ bit
+    child_type = 0 if r < parent else 1
+    half = bit >> 1
+    child0 = r - half if half > 0 else -1
+    child1 = -1
+    offset = half
+    while offset > 0:
+        if r + offset < n:
+            child1 = r + offset
+            break
+        offset >>= 1
+    return parent, child0, child1, child_type
+
+
+def dtree(n: int, r: int):
+    """The two node-level trees of node r.
+
+    Tree 0 is :func:`btree`.  Tree 1 is the same construction evaluated at a
+    relabelled index and mapped back: for odd n the index is shifted down by
+    one (mod n) and results shifted up by one; for even n the index is
+    mirrored (x -> n-1-x) both ways.  The child type of tree 1 is the one
+    computed in the relabelled coordinates.  (Section "双树：偶数 mirror，奇数
+    shift".)
+    """
+    t0 = btree(n, r)
+    if n % 2 == 1:
+        p, c0, c1, ct = btree(n, (r - 1 + n) % n)
+
+        def back(x):
+            return -1 if x == -1 else (x + 1) % n
+    else:
+        p, c0, c1, ct = btree(n, n - 1 - r)
+
+        def back(x):
+            return -1 if x == -1 else n - 1 - x
+    t1 = (back(p), back(c0), back(c1), ct)
+    return t0, t1
+
+
+def log2i(x: int) -> int:
+    """floor(log2(x)) for x >= 1."""
+    out = 0
+    while x >= 2:
+        x >>= 1
+        out += 1
+    return out
+
+
+class TopologyError(Exception):
+    """A tree record overflowed or a structural assertion failed."""
+
+
+@dataclass
+class ChannelTree:
+    """Per-rank tree records of one channel."""
+    up: list[int]
+    down: list[list[int]]
+    tree_index: int            # 0 or 1: which node-level tree this channel uses
+    depth: int                 # the pages' approximation, metadata only
+
+    @property
+    def root(self) -> int:
+        roots = [r for r, u in enumerate(self.up) if u == -1]
+        if len(roots) != 1:
+            raise TopologyError(f"expected one root, found {roots}")
+        return roots[0]
+
+    def children(self, r: int) -> list[int]:
+        return [c for c in self.down[r] if c != -1]
+
+    def true_depth(self) -> int:
+        """Longest root-to-leaf path, in edges."""
+        best = 0
+        for r in range(len(self.up)):
+            d, x = 0, r
+            while self.up[x] != -1:
+                x = self.up[x]
+                d += 1
+            best = max(best, d)
+        return best
+
+
+@dataclass
+class Topology:
+    nranks: int
+    nnodes: int
+    nchannels: int
+    channels: list[ChannelTree] = field(default_factory=list)
+
+    @property
+    def local_ranks(self) -> int:
+        return self.nranks // self.nnodes
+
+
+def _attach_up(up: list[int], r: int, parent: int) -> None:
+    if parent == -1:
+        return
+    up[r] = parent
+
+
+def _attach_down(down: list[list[int]], r: int, child: int) -> None:
+    if child == -1:
+        return
+    for slot in range(3):
+        if down[r][slot] == -1:
+            down[r][slot] = child
+            return
+    raise TopologyError(f"rank {r} has no free child slot for {child}")
+
+
+def build_topology(nranks: int, nnodes: int, nchannels: int) -> Topology:
+    """Per-channel tree records for N ranks on M nodes (L = N/M per node).
+
+    Ranks are node-major: rank = node*L + local.  Inside each node the ranks
+    form a chain in identity order (section "节点内先形成链").  The head of
+    every node is local index 0; the node-level parent and children of the
+    channel's tree are attached to it, parent first, then child0, then child1,
+    each child taking the first empty slot (section "节点间连接").
+    """
+    if nranks < 1 or nnodes < 1 or nranks % nnodes != 0:
+        raise ValueError("need nranks >= 1, nnodes >= 1 and nnodes dividing nranks")
+    if nchannels < 1:
+        raise ValueError("need at least one channel")
+    L = nranks // nnodes
+    depth = L - 1 + log2i(nnodes)
+    node_trees = [dtree(nnodes, m) for m in range(nnodes)]
+    n_first = (nchannels + 1) // 2
+    topo = Topology(nranks, nnodes, nchannels)
+    for c in range(nchannels):
+        t = 0 if c < n_first else 1
+        up = [-1] * nranks
+        down = [[-1, -1, -1] for _ in range(nranks)]
+        for node in range(nnodes):
+            for i in range(L):
+                r = node * L + i
+                up[r] = r - 1 if i > 0 else -1
+                down[r][0] = r + 1 if i < L - 1 else -1
+        for node in range(nnodes):
+            head = node * L
+            parent, child0, child1, _ = node_trees[node][t]
+            _attach_up(up, head, -1 if parent == -1 else parent * L)
+            _attach_down(down, head, -1 if child0 == -1 else child0 * L)
+            _attach_down(down, head, -1 if child1 == -1 else child1 * L)
+        topo.channels.append(ChannelTree(up, down, t, depth))
+    return topo
+
+
+def check_tree(ch: ChannelTree) -> None:
+    """The structural assertions of section "从 GRAPH 日志复原 active tree" plus
+    the arity bounds of section "数据结构不是纯二叉树".  Raises TopologyError."""
+    n = len(ch.up)
+    for r in range(n):
+        u = ch.up[r]
+        if u != -1 and r not in ch.down[u]:
+            raise TopologyError(f"rank {r}: parent {u} does not list it as a child")
+        for c in ch.children(r):
+            if ch.up[c] != r:
+                raise TopologyError(f"rank {r}: child {c} names parent {ch.up[c]}")
+    roots = [r for r in range(n) if ch.up[r] == -1]
+    if len(roots) != 1:
+        raise TopologyError(f"{len(roots)} roots")
+    edges = sum(len(ch.children(r)) for r in range(n))
+    if edges != n - 1:
+        raise TopologyError(f"{edges} edges for {n} ranks")
+    for r in range(n):
+        seen, x = set(), r
+        while ch.up[x] != -1:
+            if x in seen:
+                raise TopologyError(f"cycle through rank {x}")
+            seen.add(x)
+            x = ch.up[x]
+        if x != roots[0]:
+            raise TopologyError(f"rank {r} does not reach the root")
+    for r in range(n):
+        limit = 2 if ch.up[r] == -1 else 3
+        if len(ch.children(r)) > limit:
+            raise TopologyError(f"rank {r} has {len(ch.children(r))} children")
+
+
+def interior_nodes(n: int, which: int) -> set[int]:
+    """Node indices with at least one child in tree ``which`` of dtree(n, .).
+
+    "Interior" counts the root when it has a child: this is the reading under
+    which the probe table of section "直接执行源码中的 DTree" lists node 0 as
+    the shared interior node for odd n.
+    """
+    out = set()
+    for m in range(n):
+        _, c0, c1, _ = dtree(n, m)[which]
+        if c0 != -1 or c1 != -1:
+            out.add(m)
+    return out
+
+
+def node_tree_depth(n: int, which: int) -> int:
+    """Longest root-to-leaf path of node-level tree ``which``."""
+    best = 0
+    for m in range(n):
+        d, x = 0, m
+        while True:
+            p = dtree(n, x)[which][0]
+            if p == -1:
+                break
+            x = p
+            d += 1
+            if d > n:
+                raise TopologyError("cycle in node-level tree")
+        best = max(best, d)
+    return best
+
+
+def node_tree_root(n: int, which: int) -> int:
+    roots = [m for m in range(n) if dtree(n, m)[which][0] == -1]
+    if len(roots) != 1:
+        raise TopologyError(f"{len(roots)} node-level roots")
+    return roots[0]

@@ -1,0 +1,300 @@
+// C ABI of libemucomm: argument checks, the process-global communicator,
+// per-shape plans (device tables), and kernel launches.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <tuple>
+#include <vector>
+
+#include "common.h"
+#include "plan.h"
+#include "topology.h"
+
+namespace emu {
+
+// Defined in fused.hip / stepwise.hip.
+hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, int grid, hipStream_t stream);
+int fused_threads();
+hipError_t launch_stepwise(bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
+                           size_t lds, hipStream_t s);
+int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds);
+
+namespace {
+
+constexpr int kFusedRingFold = 0, kFusedTreeFold = 1, kFusedTreeProgram = 2;
+
+long env_long(const char* name, long fallback) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return fallback;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == '\0' && x > 0) ? x : fallback;
+}
+
+struct DeviceBuffer {
+  void* ptr = nullptr;
+  ~DeviceBuffer() { if (ptr) (void)hipFree(ptr); }
+  int upload(const void* src, size_t bytes) {
+    if (bytes == 0) return EMU_SUCCESS;
+    if (hipMalloc(&ptr, bytes) != hipSuccess) { ptr = nullptr; return EMU_ERR_HIP; }
+    if (hipMemcpy(ptr, src, bytes, hipMemcpyHostToDevice) != hipSuccess) return EMU_ERR_HIP;
+    return EMU_SUCCESS;
+  }
+};
+
+struct Plan {
+  // fused
+  DeviceBuffer tiles;
+  uint32_t ntiles = 0;
+  int fused_grid = 0;
+  // stepwise
+  DeviceBuffer tasks, table;
+  uint32_t ntasks = 0;
+  int group = 0, block = 0, grid = 0;
+  size_t lds = 0;
+  uint32_t nslices = 0, height = 0;
+};
+
+struct Comm {
+  int nranks = 0, nnodes = 0, nchannels = 0;
+  Algo algo = Algo::Ring;
+  bool fused = false;
+  size_t chunk_bytes = 0;
+  Topology topo;
+  TreeProgram prog{};
+  int tree_mode = kFusedTreeProgram;
+  // (device, count, dtype, op) -> plan
+  std::map<std::tuple<int, uint64_t, int, int>, std::unique_ptr<Plan>> plans;
+};
+
+using CommKey = std::tuple<int, int, int, int, size_t>;
+std::map<CommKey, std::unique_ptr<Comm>> g_comms;   // built communicators, reused on re-init
+Comm* g_active = nullptr;
+constexpr size_t kMaxCachedComms = 16;
+
+std::map<int, int> g_cu_count;
+
+int cu_count(int dev) {
+  auto it = g_cu_count.find(dev);
+  if (it != g_cu_count.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  g_cu_count[dev] = cus;
+  return cus;
+}
+
+int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
+  const int esz = elem_size(t);
+  const uint64_t unit = kVecBytes / esz;
+  const uint64_t chunk_count = c.chunk_bytes / esz;
+  const int cus = cu_count(dev);
+  if (c.fused) {
+    std::vector<Tile> tiles;
+    const uint64_t tile_elems = (uint64_t)fused_threads() * unit;
+    build_fused_tiles(c.topo, c.algo, count, unit, chunk_count, tile_elems, &tiles);
+    p->ntiles = (uint32_t)tiles.size();
+    if (int e = p->tiles.upload(tiles.data(), tiles.size() * sizeof(Tile))) return e;
+    const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 8);
+    p->fused_grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntiles, (uint64_t)cus * per_cu));
+    return EMU_SUCCESS;
+  }
+  const int n = c.nranks;
+  p->group = n <= 16 ? 64 : n <= 32 ? 32 : 16;
+  p->block = (n * p->group + 63) / 64 * 64;
+  const uint64_t slice_elems = (uint64_t)p->group * unit;
+  const bool ring = c.algo == Algo::Ring;
+  p->lds = (ring ? 2u : 4u) * (size_t)n * p->group * kVecBytes;
+  if (ring) {
+    std::vector<RingLoopBlock> loops;
+    std::vector<RingTask> tasks;
+    build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks);
+    p->ntasks = (uint32_t)tasks.size();
+    if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
+    if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
+  } else {
+    p->nslices = (uint32_t)env_long("EMU_TREE_SLICES", 64);
+    std::vector<TreeTask> tasks;
+    std::vector<TreeNode> nodes;
+    build_tree_tasks(c.topo, count, unit, chunk_count, p->nslices * slice_elems, &tasks, &nodes);
+    p->ntasks = (uint32_t)tasks.size();
+    uint32_t h = 0;
+    for (const auto& ch : c.topo.channels) h = std::max<uint32_t>(h, (uint32_t)ch.height);
+    p->height = h;
+    if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(TreeTask))) return e;
+    if (int e = p->table.upload(nodes.data(), nodes.size() * sizeof(TreeNode))) return e;
+  }
+  const int occ = stepwise_occupancy(ring, t, op, p->block, p->lds);
+  p->grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntasks, (uint64_t)cus * occ));
+  return EMU_SUCCESS;
+}
+
+bool valid_dtype(int d) { return d >= EMU_INT32 && d <= EMU_BFLOAT16; }
+bool valid_op(int o) { return o == EMU_SUM || o == EMU_MAX; }
+
+}  // namespace
+}  // namespace emu
+
+using namespace emu;
+
+extern "C" {
+
+int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes) {
+  const int base = algo & 0xFF;
+  const int mode = algo & ~0xFF;
+  if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE) return EMU_ERR_INVALID_ARGUMENT;
+  if (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED) return EMU_ERR_INVALID_ARGUMENT;
+  if (chunk_bytes == 0 || chunk_bytes % kVecBytes != 0 || chunk_bytes > ((size_t)1 << 40))
+    return EMU_ERR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > kMaxRanks || nnodes < 1 || nranks % nnodes != 0 || nchannels < 1 ||
+      nchannels > kMaxChannels)
+    return EMU_ERR_INVALID_ARGUMENT;
+  const CommKey key{nranks, nnodes, algo, nchannels, chunk_bytes};
+  auto it = g_comms.find(key);
+  if (it != g_comms.end()) {
+    g_active = it->second.get();
+    return EMU_SUCCESS;
+  }
+  auto c = std::make_unique<Comm>();
+  c->nranks = nranks;
+  c->nnodes = nnodes;
+  c->nchannels = nchannels;
+  c->algo = base == EMU_ALGO_RING ? Algo::Ring : Algo::Tree;
+  c->fused = mode == EMU_MODE_FUSED;
+  c->chunk_bytes = chunk_bytes;
+  if (int e = build_topology(nranks, nnodes, nchannels, &c->topo)) return e;
+  if (c->algo == Algo::Tree) {
+    // Tree 0 and tree 1 programs from the first channel of each kind.
+    bool all_pure = true;
+    for (int t = 0; t < 2; ++t) {
+      const ChannelTopology* ch = nullptr;
+      for (const auto& cc : c->topo.channels)
+        if (cc.tree_index == t) { ch = &cc; break; }
+      if (!ch) ch = &c->topo.channels[0];
+      int nregs = 0;
+      bool pure = false;
+      if (int e = compile_tree_program(*ch, c->prog.perm[t], c->prog.instr[t], &nregs, &pure)) return e;
+      c->prog.pure_fold[t] = pure ? 1 : 0;
+      c->prog.nregs[t] = (uint8_t)nregs;
+      all_pure = all_pure && pure;
+    }
+    c->tree_mode = all_pure ? kFusedTreeFold : kFusedTreeProgram;
+  }
+  if (g_comms.size() >= kMaxCachedComms) {
+    // Drop every cached communicator except the active one.
+    for (auto i = g_comms.begin(); i != g_comms.end();) {
+      if (i->second.get() == g_active) ++i;
+      else i = g_comms.erase(i);
+    }
+  }
+  g_active = c.get();
+  g_comms[key] = std::move(c);
+  return EMU_SUCCESS;
+}
+
+int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype, int op,
+                  void* stream) {
+  Comm* c = g_active;
+  if (!c) return EMU_ERR_NOT_INITIALIZED;
+  if (!valid_dtype(dtype) || !valid_op(op) || !sendbufs || !recvbufs) return EMU_ERR_INVALID_ARGUMENT;
+  const DType t = static_cast<DType>(dtype);
+  const Op o = static_cast<Op>(op);
+  const int n = c->nranks;
+  const size_t esz = (size_t)elem_size(t);
+  if (count > ((uint64_t)1 << 40) / esz) return EMU_ERR_INVALID_ARGUMENT;
+  const uint64_t bytes = (uint64_t)count * esz;
+  for (int r = 0; r < n; ++r) {
+    if (!sendbufs[r] || !recvbufs[r]) return EMU_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)sendbufs[r] | (uintptr_t)recvbufs[r]) % kVecBytes) return EMU_ERR_INVALID_ARGUMENT;
+  }
+  if (count == 0) return EMU_SUCCESS;
+  // No two distinct buffers may overlap; a rank's send and receive buffer may
+  // be the same buffer (in place).
+  std::vector<std::pair<uintptr_t, int>> spans;
+  for (int r = 0; r < n; ++r) {
+    spans.push_back({(uintptr_t)sendbufs[r], r});
+    if (recvbufs[r] != sendbufs[r]) spans.push_back({(uintptr_t)recvbufs[r], r});
+  }
+  std::sort(spans.begin(), spans.end());
+  for (size_t i = 1; i < spans.size(); ++i)
+    if (spans[i].first < spans[i - 1].first + bytes) return EMU_ERR_INVALID_ARGUMENT;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
+  const auto key = std::make_tuple(dev, (uint64_t)count, dtype, c->fused ? 0 : op);
+  auto it = c->plans.find(key);
+  if (it == c->plans.end()) {
+    auto p = std::make_unique<Plan>();
+    if (int e = make_plan(*c, dev, count, t, o, p.get())) return e;
+    it = c->plans.emplace(key, std::move(p)).first;
+  }
+  const Plan& p = *it->second;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (c->fused) {
+    FusedArgs a{};
+    for (int r = 0; r < n; ++r) { a.send[r] = sendbufs[r]; a.recv[r] = recvbufs[r]; }
+    a.tiles = static_cast<const Tile*>(p.tiles.ptr);
+    a.ntiles = p.ntiles;
+    a.nranks = (uint32_t)n;
+    a.prog = c->prog;
+    const int mode = c->algo == Algo::Ring ? kFusedRingFold : c->tree_mode;
+    err = launch_fused(t, o, mode, a, p.fused_grid, s);
+  } else {
+    StepArgs a{};
+    for (int r = 0; r < n; ++r) { a.send[r] = sendbufs[r]; a.recv[r] = recvbufs[r]; }
+    a.tasks = p.tasks.ptr;
+    a.table = p.table.ptr;
+    a.count = count;
+    a.ntasks = p.ntasks;
+    a.nranks = (uint32_t)n;
+    a.group = (uint32_t)p.group;
+    a.nslices = p.nslices;
+    a.height = p.height;
+    err = launch_stepwise(c->algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
+  }
+  return err == hipSuccess ? EMU_SUCCESS : EMU_ERR_HIP;
+}
+
+int emu_tree_topology(int channel, int rank, int* up, int down[3]) {
+  const Comm* c = g_active;
+  if (!c) return EMU_ERR_NOT_INITIALIZED;
+  if (!up || !down || channel < 0 || channel >= c->nchannels || rank < 0 || rank >= c->nranks)
+    return EMU_ERR_INVALID_ARGUMENT;
+  const RankRecord& rec = c->topo.channels[channel].ranks[rank];
+  *up = rec.up;
+  for (int s = 0; s < 3; ++s) down[s] = rec.down[s];
+  return EMU_SUCCESS;
+}
+
+int emu_tree_depth(int* depth) {
+  const Comm* c = g_active;
+  if (!c) return EMU_ERR_NOT_INITIALIZED;
+  if (!depth) return EMU_ERR_INVALID_ARGUMENT;
+  *depth = c->topo.depth_approx;
+  return EMU_SUCCESS;
+}
+
+int emu_comm_destroy(void) {
+  g_active = nullptr;
+  g_comms.clear();
+  return EMU_SUCCESS;
+}
+
+const char* emu_strerror(int code) {
+  switch (code) {
+    case EMU_SUCCESS: return "success";
+    case EMU_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case EMU_ERR_NOT_INITIALIZED: return "communicator not initialized";
+    case EMU_ERR_INTERNAL: return "internal error (topology or program check failed)";
+    case EMU_ERR_HIP: return "HIP runtime error (allocation, copy or launch)";
+    default: return "unknown error code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+// Device-side element operators on one 128-bit vector per lane.
+//
+// Every operator works lane-wise on a 16-byte vector (4 x i32/f32, 2 x i64,
+// 8 x f16/bf16) and gives the bits of the rounded binary reduction:
+//   i32/i64 sum : two's-complement wrap
+//   f32 sum     : one IEEE add, round to nearest even, subnormals kept
+//   f16 sum     : the correctly rounded f16 add (native packed f16 add)
+//   bf16 sum    : exact f32 add, then round to nearest even into bf16
+//   max         : integers plain; floats in "key" space, where the bit
+//                 pattern is mapped to a signed integer that orders -0
+//                 below +0 and otherwise follows the float order, so the
+//                 max is commutative and associative.
+// pre() maps a loaded vector into the operator's working space, post()
+// maps back before storing (identity except for float max).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "common.h"
+
+namespace emu {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef long long i64x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+template <typename T, typename U>
+__device__ __forceinline__ T bits(U v) {
+  return __builtin_bit_cast(T, v);
+}
+
+// bf16 rounding of the f32 values held in u (one per 32-bit lane): round to
+// nearest even on the upper 16 bits; NaN keeps its upper half with the quiet
+// bit set.  Result in the low 16 bits of each lane.
+__device__ __forceinline__ u32x4 bf16_round_lo(u32x4 u) {
+  const u32x4 rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const u32x4 quiet = (u >> 16) | 0x40u;
+  const i32x4 is_nan = (u & 0x7FFFFFFFu) > 0x7F800000u;   // -1 where NaN
+  const u32x4 m = bits<u32x4>(is_nan);
+  return (quiet & m) | (rounded & ~m);
+}
+
+template <DType T, Op O>
+struct Red;
+
+template <>
+struct Red<DType::I32, Op::Sum> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) { return a + b; }
+};
+template <>
+struct Red<DType::I32, Op::Max> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(__builtin_elementwise_max(bits<i32x4>(a), bits<i32x4>(b)));
+  }
+};
+template <>
+struct Red<DType::I64, Op::Sum> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(bits<i64x2>(a) + bits<i64x2>(b));
+  }
+};
+template <>
+struct Red<DType::I64, Op::Max> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(__builtin_elementwise_max(bits<i64x2>(a), bits<i64x2>(b)));
+  }
+};
+template <>
+struct Red<DType::F32, Op::Sum> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(bits<f32x4>(a) + bits<f32x4>(b));
+  }
+};
+// f32 key: negative patterns get their magnitude bits flipped, so signed
+// integer order equals float order with -0 < +0.  The map is its own inverse.
+template <>
+struct Red<DType::F32, Op::Max> {
+  static __device__ __forceinline__ u32x4 key(u32x4 x) {
+    const i32x4 s = bits<i32x4>(x);
+    return bits<u32x4>(s ^ ((s >> 31) & 0x7FFFFFFF));
+  }
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return key(x); }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return key(x); }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(__builtin_elementwise_max(bits<i32x4>(a), bits<i32x4>(b)));
+  }
+};
+template <>
+struct Red<DType::F16, Op::Sum> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(bits<f16x8>(a) + bits<f16x8>(b));
+  }
+};
+template <>
+struct Red<DType::BF16, Op::Sum> {
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    // element 0 of each 32-bit lane sits in the low half, element 1 in the high half
+    const f32x4 lo = bits<f32x4>(a << 16) + bits<f32x4>(b << 16);
+    const f32x4 hi = bits<f32x4>(a & 0xFFFF0000u) + bits<f32x4>(b & 0xFFFF0000u);
+    return bf16_round_lo(bits<u32x4>(lo)) | (bf16_round_lo(bits<u32x4>(hi)) << 16);
+  }
+};
+// 16-bit float key, same idea as the f32 key, on each half.
+struct Key16 {
+  static __device__ __forceinline__ u32x4 key(u32x4 x) {
+    const i16x8 s = bits<i16x8>(x);
+    return bits<u32x4>(s ^ ((s >> 15) & (short)0x7FFF));
+  }
+  static __device__ __forceinline__ u32x4 pre(u32x4 x) { return key(x); }
+  static __device__ __forceinline__ u32x4 post(u32x4 x) { return key(x); }
+  static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
+    return bits<u32x4>(__builtin_elementwise_max(bits<i16x8>(a), bits<i16x8>(b)));
+  }
+};
+template <>
+struct Red<DType::F16, Op::Max> : Key16 {};
+template <>
+struct Red<DType::BF16, Op::Max> : Key16 {};
+
+template <DType T>
+struct Unit {
+  static constexpr int elems = kVecBytes / (T == DType::I64 ? 8 : (T == DType::F16 || T == DType::BF16) ? 2 : 4);
+  static constexpr int esz = kVecBytes / elems;
+};
+
+// Whole-vector global accesses.  Single-use streams: non-temporal hint.
+__device__ __forceinline__ u32x4 ld_vec(const void* base, uint64_t byte_off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off));
+}
+__device__ __forceinline__ void st_vec(void* base, uint64_t byte_off, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off));
+}
+
+// Partial vector at the very end of a buffer: `nbytes` (< 16, a multiple of
+// 2) valid bytes, read and written 16 bits at a time; the rest is zero.
+__device__ __forceinline__ u32x4 ld_part(const void* base, uint64_t byte_off, int nbytes) {
+  const uint16_t* p = reinterpret_cast<const uint16_t*>(static_cast<const char*>(base) + byte_off);
+  u32x4 v = {0, 0, 0, 0};
+#pragma unroll 1
+  for (int i = 0; 2 * i < nbytes; ++i) {
+    const uint32_t h = (uint32_t)p[i] << (16 * (i & 1));
+    if (i < 2) v.x |= h;
+    else if (i < 4) v.y |= h;
+    else if (i < 6) v.z |= h;
+    else v.w |= h;
+  }
+  return v;
+}
+__device__ __forceinline__ void st_part(void* base, uint64_t byte_off, int nbytes, u32x4 v) {
+  uint16_t* p = reinterpret_cast<uint16_t*>(static_cast<char*>(base) + byte_off);
+#pragma unroll 1
+  for (int i = 0; 2 * i < nbytes; ++i) {
+    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+    p[i] = (uint16_t)(w >> (16 * (i & 1)));
+  }
+}
+
+// Load / store `nbytes` of one vector (16 = whole vector).
+__device__ __forceinline__ u32x4 ld_any(const void* base, uint64_t byte_off, int nbytes) {
+  return nbytes == kVecBytes ? ld_vec(base, byte_off) : ld_part(base, byte_off, nbytes);
+}
+__device__ __forceinline__ void st_any(void* base, uint64_t byte_off, int nbytes, u32x4 v) {
+  if (nbytes == kVecBytes) st_vec(base, byte_off, v);
+  else st_part(base, byte_off, nbytes, v);
+}
+
+}  // namespace emu

@@ -1,0 +1,53 @@
+// Host topology builder: node-level double binary tree, intra-node chain,
+// head mapping, per-channel tree records.
+#pragma once
+
+#include <array>
+#include <vector>
+
+#include "common.h"
+
+namespace emu {
+
+struct NodeTreeEdges {
+  int parent;      // -1 at the root
+  int child0;      // -1 if absent
+  int child1;      // -1 if absent
+  int child_type;  // 0: below its parent, 1: above; -1 at the root
+};
+
+// Binary tree over node indices 0..n-1 (page "NCCL 专家课程 13", section
+// "Btree 的 bit 构造").
+NodeTreeEdges node_btree(int n, int r);
+// Tree 0 and tree 1 of the double binary tree (section "双树：偶数 mirror，
+// 奇数 shift").
+std::array<NodeTreeEdges, 2> node_dtree(int n, int r);
+
+struct RankRecord {
+  int up = -1;
+  int down[3] = {-1, -1, -1};
+};
+
+struct ChannelTopology {
+  int tree_index = 0;               // which node-level tree
+  std::vector<RankRecord> ranks;    // per rank
+  std::vector<int> depth;           // distance from the root, per rank
+  int root = 0;
+  int height = 0;                   // max depth
+};
+
+struct Topology {
+  int nranks = 0, nnodes = 0, nchannels = 0;
+  int depth_approx = 0;             // nranks/nnodes - 1 + floor(log2 nnodes)
+  std::vector<ChannelTopology> channels;
+};
+
+// Builds and validates; returns EMU_SUCCESS, EMU_ERR_INVALID_ARGUMENT or
+// EMU_ERR_INTERNAL (record overflow or a failed structural check).
+int build_topology(int nranks, int nnodes, int nchannels, Topology* out);
+
+// Structural checks: parent/child symmetry, one root, N-1 edges, no cycle,
+// every rank reaches the root, at most 2 children at the root and 3 elsewhere.
+bool check_channel(const ChannelTopology& ch);
+
+}  // namespace emu

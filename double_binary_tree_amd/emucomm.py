@@ -1,0 +1,130 @@
+"""Thin ctypes binding of libemucomm (declared in include/emu_comm.h).
+
+Argument marshalling only: every step of the all-reduce runs in the
+library's HIP kernels.  The library is loaded on first use; a missing
+library raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libemucomm.so")
+
+ALGO = {"ring": 0, "tree": 1}
+MODE = {"stepwise": 0x000, "fused": 0x100}
+DTYPE = {"i32": 0, "i64": 1, "f32": 2, "f16": 3, "bf16": 4}
+OP = {"sum": 0, "max": 1}
+ITEMSIZE = {"i32": 4, "i64": 8, "f32": 4, "f16": 2, "bf16": 2}
+
+SUCCESS = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_NOT_INITIALIZED = 2
+ERR_INTERNAL = 3
+ERR_HIP = 4
+
+_lib = None
+
+
+class EmuError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+        L = ctypes.CDLL(LIB_PATH)
+        L.emu_comm_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t]
+        L.emu_comm_init.restype = ctypes.c_int
+        L.emu_allreduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                    ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_allreduce.restype = ctypes.c_int
+        L.emu_tree_topology.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_int)]
+        L.emu_tree_topology.restype = ctypes.c_int
+        L.emu_tree_depth.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        L.emu_tree_depth.restype = ctypes.c_int
+        L.emu_comm_destroy.argtypes = []
+        L.emu_comm_destroy.restype = ctypes.c_int
+        L.emu_strerror.argtypes = [ctypes.c_int]
+        L.emu_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().emu_strerror(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != SUCCESS:
+        raise EmuError(code, what)
+
+
+def algo_code(algo: str, mode: str = "stepwise") -> int:
+    return ALGO[algo] | MODE[mode]
+
+
+def comm_init_raw(nranks: int, nnodes: int, algo: int, nchannels: int, chunk_bytes: int) -> int:
+    return lib().emu_comm_init(nranks, nnodes, algo, nchannels, chunk_bytes)
+
+
+def comm_init(nranks: int, nnodes: int, algo: str, nchannels: int, chunk_bytes: int,
+              mode: str = "stepwise") -> None:
+    _check(comm_init_raw(nranks, nnodes, algo_code(algo, mode), nchannels, chunk_bytes), "emu_comm_init")
+
+
+def allreduce_raw(sendptrs, recvptrs, count: int, dtype: int, op: int, stream: int = 0) -> int:
+    n = len(sendptrs)
+    send = (ctypes.c_void_p * max(n, 1))(*[ctypes.c_void_p(int(p)) for p in sendptrs])
+    recv = (ctypes.c_void_p * max(len(recvptrs), 1))(*[ctypes.c_void_p(int(p)) for p in recvptrs])
+    return lib().emu_allreduce(send, recv, count, dtype, op, ctypes.c_void_p(int(stream)))
+
+
+def allreduce(sendptrs, recvptrs, count: int, dtype: str, op: str, stream: int = 0) -> None:
+    _check(allreduce_raw(sendptrs, recvptrs, count, DTYPE[dtype], OP[op], stream), "emu_allreduce")
+
+
+def tree_topology(channel: int, rank: int) -> tuple[int, list[int]]:
+    up = ctypes.c_int(0)
+    down = (ctypes.c_int * 3)()
+    _check(lib().emu_tree_topology(channel, rank, ctypes.byref(up), down), "emu_tree_topology")
+    return up.value, list(down)
+
+
+def tree_depth() -> int:
+    d = ctypes.c_int(0)
+    _check(lib().emu_tree_depth(ctypes.byref(d)), "emu_tree_depth")
+    return d.value
+
+
+def comm_destroy() -> None:
+    _check(lib().emu_comm_destroy(), "emu_comm_destroy")
+
+
+# --- torch convenience (device memory and streams only) ---------------------
+
+def torch_dtype_name(t) -> str:
+    import torch
+    return {torch.int32: "i32", torch.int64: "i64", torch.float32: "f32",
+            torch.float16: "f16", torch.bfloat16: "bf16"}[t.dtype]
+
+
+def allreduce_tensors(sends, recvs, op: str = "sum", stream=None) -> None:
+    """All-reduce a list of per-rank CUDA tensors (same shape and dtype,
+    contiguous) into ``recvs`` on ``stream`` (default: the current stream)."""
+    import torch
+    if len(sends) != len(recvs) or not sends:
+        raise ValueError("need one send and one receive tensor per rank")
+    dt = torch_dtype_name(sends[0])
+    count = sends[0].numel()
+    for t in list(sends) + list(recvs):
+        if not t.is_cuda or not t.is_contiguous() or t.numel() != count or torch_dtype_name(t) != dt:
+            raise ValueError("tensors must be contiguous CUDA tensors of one shape and dtype")
+    s = torch.cuda.current_stream() if stream is None else stream
+    allreduce([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count, dt, op, s.cuda_stream)

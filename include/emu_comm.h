@@ -1,0 +1,152 @@
+/*
+ * emu_comm.h - C ABI of libemucomm: an all-reduce data-path emulator for
+ * N virtual ranks whose buffers all live in one GPU's HBM (AMD MI355X,
+ * gfx950).
+ *
+ * The operation is the all-reduce of the NCCL public call as described on
+ * the page "NCCL 内部机制：一次 AllReduce 如何变成拓扑图、Channel 与 GPU
+ * Kernel" (section on the public API: send buffer, receive buffer, element
+ * count, data type, reduction operator, communicator, stream; the call only
+ * enqueues work on the stream).  Here every virtual rank has its own send and
+ * receive buffer and one call reduces all of them.  The schedules are those
+ * of "NCCL 专家课程 13：Tree、双树、层次化连接与真实交叉区间" (tree
+ * reduce-up / broadcast-down, sections "先固定方向" and "runTreeSplit 如何流水";
+ * double binary tree, section "双树：偶数 mirror，奇数 shift"; intra-node chain,
+ * section "节点内先形成链") and of "all-reduce 每张卡要发多少数据? ring 和 tree
+ * 有什么区别?" (ring reduce-scatter + all-gather, Figure 1 and section "手撕
+ * 代码").
+ *
+ * One process-global communicator (the calls take no handle).  Not
+ * thread-safe: the caller serialises calls.  Every function returns an
+ * emu_result code; nothing throws or aborts across this boundary.
+ */
+#ifndef EMU_COMM_H
+#define EMU_COMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Algorithms (low byte of `algo`).  TREE on one node is the intra-node
+ * chain; on several nodes it is the chain inside each node plus the double
+ * binary tree across node heads (local rank 0 of every node). */
+#define EMU_ALGO_RING 0
+#define EMU_ALGO_TREE 1
+/* Execution mode, OR-ed into `algo`.
+ * STEPWISE (default): every ring step / tree hop runs as a receive-reduce-
+ *   copy between virtual ranks through step FIFO slots, as the pages'
+ *   primitives do.
+ * FUSED: one pass that reads every rank's input once, evaluates each
+ *   element in the schedule's exact order, and writes every rank's output.
+ * Both give bit-identical results. */
+#define EMU_MODE_STEPWISE 0x000
+#define EMU_MODE_FUSED 0x100
+
+/* Element types. */
+#define EMU_INT32 0
+#define EMU_INT64 1
+#define EMU_FLOAT32 2
+#define EMU_FLOAT16 3
+#define EMU_BFLOAT16 4
+
+/* Reduction operators.  Sum: integers wrap; floats are rounded to the
+ * buffer type after every hop (f16/bf16: exact f32 add, then round to
+ * nearest even).  Max: float max orders -0 below +0, so its result does not
+ * depend on the order. */
+#define EMU_SUM 0
+#define EMU_MAX 1
+
+/* Result codes. */
+#define EMU_SUCCESS 0
+#define EMU_ERR_INVALID_ARGUMENT 1
+#define EMU_ERR_NOT_INITIALIZED 2
+#define EMU_ERR_INTERNAL 3
+#define EMU_ERR_HIP 4
+
+/* Limits. */
+#define EMU_MAX_RANKS 64
+#define EMU_MAX_CHANNELS 64
+
+/*
+ * emu_comm_init - build the communicator: per-channel tree records for
+ * `nranks` virtual ranks on `nnodes` nodes (ranks are node-major:
+ * rank = node * (nranks/nnodes) + local), the channel count and the chunk
+ * size.
+ *   nranks      1..EMU_MAX_RANKS
+ *   nnodes      >= 1, divides nranks
+ *   algo        EMU_ALGO_RING or EMU_ALGO_TREE, optionally | EMU_MODE_FUSED
+ *   nchannels   1..EMU_MAX_CHANNELS.  The message is split into nchannels
+ *               disjoint ranges (page "NCCL 专家课程 13", section "前置知识");
+ *               the first ceil(nchannels/2) channels use tree 0, the others
+ *               tree 1 (the duplicated channel records of section "节点内先
+ *               形成链").
+ *   chunk_bytes > 0, a multiple of 16.  Tree: chunk size inside a channel;
+ *               ring: each loop covers nranks chunks.
+ * Host only: touches no GPU (device resources are created on the first
+ * emu_allreduce).  Replaces any previous communicator.
+ * Errors: EMU_ERR_INVALID_ARGUMENT for out-of-range arguments (state left
+ * unchanged); EMU_ERR_INTERNAL if a tree record overflows (cannot happen
+ * within the limits above).
+ */
+int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes);
+
+/*
+ * emu_allreduce - enqueue one all-reduce on `stream` (a hipStream_t; NULL is
+ * the default stream) and return.  Completion is observed by synchronising
+ * the stream.
+ *   sendbufs  host array of nranks device pointers; sendbufs[r] holds
+ *             `count` elements of virtual rank r
+ *   recvbufs  host array of nranks device pointers, the outputs; after
+ *             completion every recvbufs[r][0..count) holds the same bits.
+ *             recvbufs[r] == sendbufs[r] (in place) is allowed; any other
+ *             overlap between buffers is invalid.
+ *   count     elements per rank; 0 is a successful no-op
+ *   dtype     EMU_INT32 .. EMU_BFLOAT16;  op  EMU_SUM or EMU_MAX
+ * Every pointer must be non-NULL and 16-byte aligned.  The host arrays are
+ * read during the call only; the device buffers must stay alive until the
+ * stream work completes.  The caller owns all buffers and the stream; the
+ * library owns its tables and device workspace.
+ * Errors (checked before anything is enqueued): EMU_ERR_NOT_INITIALIZED,
+ * EMU_ERR_INVALID_ARGUMENT; EMU_ERR_HIP when the runtime refuses an
+ * allocation, copy or launch.  Faults inside kernels surface at the stream
+ * synchronisation.
+ */
+int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count,
+                  int dtype, int op, void* stream);
+
+/*
+ * emu_tree_topology - the tree record of `rank` in `channel`: its parent
+ * (*up, -1 at the root) and its three child slots (down[0..2], -1 when
+ * empty), in the order they were filled (intra-node child first, then the
+ * node-level child0, then child1).  Mirrors the tree record of page "NCCL
+ * 专家课程 13", section "数据结构不是纯二叉树".  Valid after emu_comm_init
+ * for either algorithm.  Host only.
+ * Errors: EMU_ERR_NOT_INITIALIZED; EMU_ERR_INVALID_ARGUMENT for a channel or
+ * rank out of range or a NULL pointer.
+ */
+int emu_tree_topology(int channel, int rank, int* up, int down[3]);
+
+/*
+ * emu_tree_depth - the depth field of the tree records: the pages'
+ * approximation nranks/nnodes - 1 + floor(log2(nnodes)) (section "节点间
+ * 连接"), metadata only.  Errors: EMU_ERR_NOT_INITIALIZED, NULL pointer.
+ */
+int emu_tree_depth(int* depth);
+
+/*
+ * emu_comm_destroy - free the communicator and every device resource the
+ * library allocated.  Call with no work of the library pending on any
+ * stream.  Destroying when nothing is initialised succeeds.
+ */
+int emu_comm_destroy(void);
+
+/* emu_strerror - static description of a result code (never NULL). */
+const char* emu_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EMU_COMM_H */

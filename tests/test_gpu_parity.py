@@ -1,0 +1,126 @@
+"""Parity of the HIP all-reduce (through the C ABI) with the CPU oracle.
+
+Bar: bit-exact for every element type, since the kernels evaluate every
+element in the oracle's own order (integers: exact; floats: order-matched
+with per-hop rounding).  Float results are also held to the float64 bound.
+"""
+
+import numpy as np
+import pytest
+
+from double_binary_tree_amd import inputs as I
+from oracle import allreduce as A
+from tests.gpu_util import announce, run_allreduce
+
+pytestmark = pytest.mark.gpu
+
+RTOL = {"f32": 1e-5, "f16": 1e-2, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from double_binary_tree_amd import emucomm as E
+    E.lib()   # a missing library is an error on a GPU machine
+    yield
+    E.comm_destroy()
+
+
+def _bits(x):
+    return np.ascontiguousarray(x).view(np.uint8)
+
+
+def _check(w, algo, mode, count, chunk_bytes, inplace, salt=0):
+    announce(f"{w.name} algo={algo} mode={mode} count={count} chunk={chunk_bytes} inplace={inplace}")
+    xs = I.rank_inputs(w, count=count, salt=salt)
+    want = A.allreduce(xs, w.nnodes, algo, w.nchannels, chunk_bytes, w.dtype, w.op)[0]
+    got, _ = run_allreduce(xs, w.nnodes, algo, mode, w.nchannels, chunk_bytes, w.dtype, w.op, inplace)
+    wb = _bits(want).reshape(len(want), -1)
+    for r, g in enumerate(got):
+        gb = _bits(g).reshape(len(g), -1)
+        if not np.array_equal(gb, wb):
+            first = np.nonzero((gb != wb).any(axis=1))[0]
+            raise AssertionError(f"rank {r}: {len(first)} elements differ, first at {first[:8].tolist()}"
+                                 f" got {g[first[:4]]} want {want[first[:4]]}")
+    if w.dtype in RTOL and w.op == "sum":
+        ok, err = A.within_tolerance(got[0], xs, w.dtype, RTOL[w.dtype])
+        assert ok, err
+
+
+CASES = []
+for name, w in I.WORKLOADS.items():
+    for algo in w.algos:
+        for mode in ("fused", "stepwise"):
+            CASES.append((name, algo, mode))
+
+
+@pytest.mark.parametrize("name,algo,mode", CASES)
+@pytest.mark.parametrize("inplace", [False, True])
+def test_parity_small_chunks(name, algo, mode, inplace):
+    # Small chunks so that a modest count spans many chunks, ring loops,
+    # tiles and workgroup tasks, with a ragged tail.
+    w = I.WORKLOADS[name]
+    unit = 16 // w.itemsize
+    count = 37 * 1024 + 3 * unit + (1 if unit > 1 else 0)
+    _check(w, algo, mode, count, chunk_bytes=4096, inplace=inplace)
+
+
+@pytest.mark.parametrize("name,algo,mode", CASES)
+def test_parity_workload_chunk(name, algo, mode):
+    # The workload's own chunk size at a count the oracle finishes quickly.
+    w = I.WORKLOADS[name]
+    count = min(w.count, 300_000 + 5)
+    _check(w, algo, mode, count, chunk_bytes=w.chunk_bytes, inplace=False, salt=1)
+
+
+EDGE_COUNTS = [1, 2, 3, 7, 8, 9, 15, 16, 17, 255, 256, 257, 1023, 1024, 1025, 4099]
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+@pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("bf16", "sum"), ("f16", "max"), ("i64", "sum")])
+def test_edge_counts(algo, mode, dtype, op):
+    base = I.Workload("edge", 7, 6, 3, (algo,), 5, 64, dtype, op, 1,
+                      ("int", -50, 50) if dtype.startswith("i") else ("normal", 1.0))
+    for count in EDGE_COUNTS:
+        _check(base, algo, mode, count, chunk_bytes=64, inplace=(count % 2 == 1))
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+@pytest.mark.parametrize("n,m,nch", [(1, 1, 1), (2, 1, 1), (2, 2, 3), (3, 3, 2), (5, 5, 7),
+                                     (12, 3, 4), (17, 17, 2), (24, 4, 6), (33, 3, 3), (64, 8, 64),
+                                     (64, 64, 2), (48, 2, 1)])
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+def test_shapes(n, m, nch, algo, mode):
+    w = I.Workload("shape", 8, n, m, (algo,), nch, 256, "f32", "sum", 1, ("normal", 1.0))
+    _check(w, algo, mode, 6 * 1024 + 13, chunk_bytes=256, inplace=False)
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise"])
+def test_count_zero_is_noop(mode):
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    E.comm_init(4, 2, "tree", 2, 4096, mode=mode)
+    sends = [torch.full((8,), float(r), device="cuda") for r in range(4)]
+    recvs = [torch.full((8,), -1.0, device="cuda") for _ in range(4)]
+    E.allreduce([s.data_ptr() for s in sends], [r.data_ptr() for r in recvs], 0, "f32", "sum",
+                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert all(bool((r == -1.0).all()) for r in recvs)
+
+
+@pytest.mark.parametrize("algo,mode", [("ring", "fused"), ("tree", "fused"), ("ring", "stepwise"),
+                                       ("tree", "stepwise")])
+def test_deterministic_and_modes_agree(algo, mode):
+    w = I.WORKLOADS["hier4x8_f16"] if algo == "tree" else I.WORKLOADS["chain8_f32"]
+    xs = I.rank_inputs(w, count=200_003, salt=2)
+    announce(f"determinism {w.name} {algo} {mode}")
+    a, sends = run_allreduce(xs, w.nnodes, algo, mode, w.nchannels, w.chunk_bytes, w.dtype, w.op)
+    b, _ = run_allreduce(xs, w.nnodes, algo, mode, w.nchannels, w.chunk_bytes, w.dtype, w.op, sends=sends)
+    other = "stepwise" if mode == "fused" else "fused"
+    c, _ = run_allreduce(xs, w.nnodes, algo, other, w.nchannels, w.chunk_bytes, w.dtype, w.op, sends=sends)
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(_bits(x), _bits(y))
+        assert np.array_equal(_bits(x), _bits(z))

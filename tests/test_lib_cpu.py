@@ -1,0 +1,128 @@
+"""Host-side checks of libemucomm (no GPU): the library loads, exports every
+function include/emu_comm.h declares, builds the same tree records as the
+oracle topology, and rejects bad arguments before touching a device."""
+
+import os
+import re
+
+import pytest
+
+from double_binary_tree_amd import emucomm as E
+from oracle import topology as T
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "emu_comm.h")
+
+
+@pytest.fixture(autouse=True)
+def _fresh():
+    E.comm_destroy()
+    yield
+    E.comm_destroy()
+
+
+def test_exports_every_declared_function():
+    text = open(HEADER, encoding="utf-8").read()
+    names = re.findall(r"^\s*(?:int|const char\s*\*)\s*(emu_\w+)\s*\(", text, flags=re.M)
+    assert len(names) >= 6
+    L = E.lib()
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER, encoding="utf-8").read()
+    consts = dict(re.findall(r"#define\s+(EMU_\w+)\s+(0x[0-9A-Fa-f]+|\d+)", text))
+    val = {k: int(v, 0) for k, v in consts.items()}
+    assert val["EMU_ALGO_RING"] == E.ALGO["ring"] and val["EMU_ALGO_TREE"] == E.ALGO["tree"]
+    assert val["EMU_MODE_FUSED"] == E.MODE["fused"] and val["EMU_MODE_STEPWISE"] == E.MODE["stepwise"]
+    for k, name in (("EMU_INT32", "i32"), ("EMU_INT64", "i64"), ("EMU_FLOAT32", "f32"),
+                    ("EMU_FLOAT16", "f16"), ("EMU_BFLOAT16", "bf16")):
+        assert val[k] == E.DTYPE[name]
+    assert val["EMU_SUM"] == E.OP["sum"] and val["EMU_MAX"] == E.OP["max"]
+
+
+def _shapes():
+    for n in range(1, 65):
+        for m in range(1, n + 1):
+            if n % m == 0 and (n <= 12 or m in (1, 2, 3, 4, n // 8 if n % 8 == 0 else 1, n)):
+                yield n, m
+
+
+def test_topology_matches_oracle():
+    checked = 0
+    for n, m in _shapes():
+        for nch in (1, 2, 5, 16):
+            E.comm_init(n, m, "tree", nch, 1 << 19)
+            ref = T.build_topology(n, m, nch)
+            assert E.tree_depth() == ref.channels[0].depth
+            for c in range(nch):
+                for r in range(n):
+                    up, down = E.tree_topology(c, r)
+                    assert up == ref.channels[c].up[r], (n, m, nch, c, r)
+                    assert down == ref.channels[c].down[r], (n, m, nch, c, r)
+                    checked += 1
+    assert checked > 20000
+
+
+def test_ring_comm_also_reports_topology():
+    E.comm_init(8, 1, "ring", 12, 1 << 19, mode="fused")
+    assert E.tree_topology(0, 0) == (-1, [1, -1, -1])
+    assert E.tree_topology(11, 7) == (6, [-1, -1, -1])
+
+
+def test_init_rejects_bad_arguments_and_keeps_state():
+    E.comm_init(4, 2, "tree", 2, 1 << 19)
+    bad = [
+        (0, 1, 1, 1, 1 << 19), (65, 1, 1, 1, 1 << 19), (4, 3, 1, 1, 1 << 19), (4, 0, 1, 1, 1 << 19),
+        (4, 1, 1, 0, 1 << 19), (4, 1, 1, 65, 1 << 19), (4, 1, 1, 1, 0), (4, 1, 1, 1, 24),
+        (4, 1, 7, 1, 1 << 19), (4, 1, 0x201, 1, 1 << 19),
+    ]
+    for args in bad:
+        assert E.comm_init_raw(*args) == E.ERR_INVALID_ARGUMENT, args
+    # the previous communicator is still active
+    up, down = E.tree_topology(0, 2)
+    ref = T.build_topology(4, 2, 2).channels[0]
+    assert (up, down) == (ref.up[2], ref.down[2])
+
+
+def test_calls_before_init():
+    assert E.allreduce_raw([16], [32], 4, 0, 0) == E.ERR_NOT_INITIALIZED
+    with pytest.raises(E.EmuError) as ei:
+        E.tree_topology(0, 0)
+    assert ei.value.code == E.ERR_NOT_INITIALIZED
+    assert E.lib().emu_tree_depth(None) == E.ERR_NOT_INITIALIZED
+
+
+def test_topology_argument_errors():
+    E.comm_init(4, 1, "tree", 2, 1 << 19)
+    for c, r in ((-1, 0), (2, 0), (0, -1), (0, 4)):
+        with pytest.raises(E.EmuError) as ei:
+            E.tree_topology(c, r)
+        assert ei.value.code == E.ERR_INVALID_ARGUMENT
+
+
+def test_allreduce_argument_errors_without_gpu():
+    # All of these are rejected before any device call, so they run on CPU.
+    E.comm_init(2, 1, "ring", 1, 1 << 19, mode="fused")
+    base = 1 << 32
+    ok_send, ok_recv = [base, base + 4096], [base + 8192, base + 12288]
+    raw = E.allreduce_raw
+    assert raw(ok_send, ok_recv, 16, 9, 0) == E.ERR_INVALID_ARGUMENT          # dtype
+    assert raw(ok_send, ok_recv, 16, 2, 5) == E.ERR_INVALID_ARGUMENT          # op
+    assert raw([base + 8, base + 4096], ok_recv, 16, 2, 0) == E.ERR_INVALID_ARGUMENT  # alignment
+    assert raw([0, base + 4096], ok_recv, 16, 2, 0) == E.ERR_INVALID_ARGUMENT         # null
+    # rank 1's send overlaps rank 0's send
+    assert raw([base, base + 16], ok_recv, 16, 2, 0) == E.ERR_INVALID_ARGUMENT
+    # a receive buffer partly overlapping its own send buffer
+    assert raw(ok_send, [base + 16, base + 12288], 16, 2, 0) == E.ERR_INVALID_ARGUMENT
+    # count 0 is a no-op, in place is fine
+    assert raw(ok_send, ok_recv, 0, 2, 0) == E.SUCCESS
+    assert raw(ok_send, ok_send, 0, 2, 0) == E.SUCCESS
+    # absurd count
+    assert raw(ok_send, ok_recv, 1 << 62, 2, 0) == E.ERR_INVALID_ARGUMENT
+
+
+def test_strerror_total():
+    for code in range(-1, 7):
+        assert isinstance(E.strerror(code), str) and E.strerror(code)

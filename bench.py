@@ -61,24 +61,29 @@ def traffic_from_profiles(leg_key: str):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, n_sample: int) -> dict:
-    """The oracle as it stands, timed on the host on a bounded sample."""
-    import numpy as np
+def cpu_baseline(w, n_sample: int, min_seconds: float) -> dict:
+    """The oracle as it stands, timed on the host: ring + tree all-reduce of
+    the workload (n_sample elements per rank), repeated until min_seconds
+    have passed (at least once)."""
     from double_binary_tree_amd import inputs as I
     from oracle import allreduce as A
 
     xs = I.rank_inputs(w, count=n_sample)
+    reps = 0
     t0 = time.perf_counter()
-    for algo in ("ring", "tree"):
-        A.allreduce(xs, w.nnodes, algo, w.nchannels, w.chunk_bytes, w.dtype, w.op)
-    t = time.perf_counter() - t0
+    while True:
+        for algo in ("ring", "tree"):
+            A.allreduce(xs, w.nnodes, algo, w.nchannels, w.chunk_bytes, w.dtype, w.op)
+        reps += 1
+        t = time.perf_counter() - t0
+        if t >= min_seconds:
+            break
     s_bytes = n_sample * w.itemsize
-    busbw = 2 * s_bytes * 2 * (w.nranks - 1) / w.nranks / t / 1e9
-    del np
+    busbw = reps * 2 * s_bytes * 2 * (w.nranks - 1) / w.nranks / t / 1e9
     return {"value": round(busbw, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"oracle ring + tree all-reduce of the same workload shape on {n_sample} "
-                      f"f32 elements per rank ({w.nranks} ranks, {w.nchannels} channels), numpy, "
-                      f"one thread; {t:.2f} s"}
+            "sample": f"oracle (numpy, one thread) ring + tree all-reduce of the bench workload, "
+                      f"{n_sample} f32 elements per rank x {w.nranks} ranks, {w.nchannels} channels; "
+                      f"{reps} repetition(s) in {t:.1f} s; busbw of the same step definition"}
 
 
 def main() -> int:
@@ -87,8 +92,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--leg-iters", type=int, default=20)
-    ap.add_argument("--cpu-sample", type=int, default=4 * 1024 * 1024)
+    ap.add_argument("--cpu-sample", type=int, default=16 * 1024 * 1024)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-kernel", action="store_true",
+                    help="also run one elementwise multiply over 512 MiB (read) + 512 MiB (write), "
+                         "the known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the emulated ranks all live in one GPU's HBM; "
@@ -175,6 +184,9 @@ def main() -> int:
     end.synchronize()
     t_copy = start.elapsed_time(end) / 1e3 / 10
     copy_gbps = 2 * n * s_bytes / t_copy / 1e9
+    if args.calibration_kernel:
+        torch.mul(big, 1.0, out=big2)
+        torch.cuda.synchronize()
     del big, big2
 
     # The timed steps.
@@ -221,7 +233,7 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_seconds)
     print(json.dumps(out), flush=True)
     E.comm_destroy()
     return 0

@@ -19,10 +19,11 @@ namespace emu {
 
 // Defined in fused.hip / stepwise.hip.
 hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, int grid, hipStream_t stream);
-int fused_threads();
+int fused_tile_vectors();
 hipError_t launch_stepwise(bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
                            size_t lds, hipStream_t s);
 int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds);
+int stepwise_vectors_per_lane(bool ring);
 
 namespace {
 
@@ -78,6 +79,17 @@ Comm* g_active = nullptr;
 constexpr size_t kMaxCachedComms = 16;
 
 std::map<int, int> g_cu_count;
+std::map<int, size_t> g_lds_limit;
+
+size_t lds_per_block(int dev) {
+  auto it = g_lds_limit.find(dev);
+  if (it != g_lds_limit.end()) return it->second;
+  int bytes = 0;
+  if (hipDeviceGetAttribute(&bytes, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || bytes <= 0)
+    bytes = 65536;
+  g_lds_limit[dev] = (size_t)bytes;
+  return (size_t)bytes;
+}
 
 int cu_count(int dev) {
   auto it = g_cu_count.find(dev);
@@ -96,29 +108,37 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   const int cus = cu_count(dev);
   if (c.fused) {
     std::vector<Tile> tiles;
-    const uint64_t tile_elems = (uint64_t)fused_threads() * unit;
+    const uint64_t tile_elems = (uint64_t)fused_tile_vectors() * unit;
     build_fused_tiles(c.topo, c.algo, count, unit, chunk_count, tile_elems, &tiles);
     p->ntiles = (uint32_t)tiles.size();
     if (int e = p->tiles.upload(tiles.data(), tiles.size() * sizeof(Tile))) return e;
-    const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 8);
+    const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 32);
     p->fused_grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntiles, (uint64_t)cus * per_cu));
     return EMU_SUCCESS;
   }
   const int n = c.nranks;
-  p->group = n <= 16 ? 64 : n <= 32 ? 32 : 16;
-  p->block = (n * p->group + 63) / 64 * 64;
-  const uint64_t slice_elems = (uint64_t)p->group * unit;
   const bool ring = c.algo == Algo::Ring;
-  p->lds = (ring ? 2u : 4u) * (size_t)n * p->group * kVecBytes;
+  const int vpl = stepwise_vectors_per_lane(ring);
+  // Lanes per virtual rank: the widest group that fits one workgroup
+  // (N*G <= 1024 threads) and the device's LDS per workgroup.
+  const size_t lds_limit = lds_per_block(dev);
+  p->group = 64;
+  auto lds_of = [&](int g) { return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes; };
+  while (p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
+  if (n * p->group > 1024 || lds_of(p->group) > lds_limit) return EMU_ERR_INTERNAL;
+  p->block = (n * p->group + 63) / 64 * 64;
+  const uint64_t slice_elems = (uint64_t)p->group * vpl * unit;
+  p->lds = lds_of(p->group);
   if (ring) {
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
+    if (count / slice_elems >= ((uint64_t)1 << 32)) return EMU_ERR_INVALID_ARGUMENT;   // cell index is 32-bit
     build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks);
     p->ntasks = (uint32_t)tasks.size();
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
     if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
   } else {
-    p->nslices = (uint32_t)env_long("EMU_TREE_SLICES", 64);
+    p->nslices = (uint32_t)env_long("EMU_TREE_SLICES", 32);
     std::vector<TreeTask> tasks;
     std::vector<TreeNode> nodes;
     build_tree_tasks(c.topo, count, unit, chunk_count, p->nslices * slice_elems, &tasks, &nodes);
@@ -149,7 +169,7 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
   const int mode = algo & ~0xFF;
   if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE) return EMU_ERR_INVALID_ARGUMENT;
   if (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED) return EMU_ERR_INVALID_ARGUMENT;
-  if (chunk_bytes == 0 || chunk_bytes % kVecBytes != 0 || chunk_bytes > ((size_t)1 << 40))
+  if (chunk_bytes == 0 || chunk_bytes % kVecBytes != 0 || chunk_bytes > ((size_t)1 << 30))
     return EMU_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks || nnodes < 1 || nranks % nnodes != 0 || nchannels < 1 ||
       nchannels > kMaxChannels)
@@ -186,7 +206,11 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
     c->tree_mode = all_pure ? kFusedTreeFold : kFusedTreeProgram;
   }
   if (g_comms.size() >= kMaxCachedComms) {
-    // Drop every cached communicator except the active one.
+    // Drop every cached communicator except the active one.  Their device
+    // tables may still be read by enqueued kernels: wait for the device first.
+    bool has_plans = false;
+    for (const auto& kv : g_comms) has_plans = has_plans || !kv.second->plans.empty();
+    if (has_plans) (void)hipDeviceSynchronize();
     for (auto i = g_comms.begin(); i != g_comms.end();) {
       if (i->second.get() == g_active) ++i;
       else i = g_comms.erase(i);
@@ -281,6 +305,9 @@ int emu_tree_depth(int* depth) {
 }
 
 int emu_comm_destroy(void) {
+  bool has_plans = false;
+  for (const auto& kv : g_comms) has_plans = has_plans || !kv.second->plans.empty();
+  if (has_plans) (void)hipDeviceSynchronize();
   g_active = nullptr;
   g_comms.clear();
   return EMU_SUCCESS;

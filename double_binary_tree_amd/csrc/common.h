@@ -63,7 +63,7 @@ struct FusedArgs {
 struct RingLoopBlock {
   uint64_t offset;
   uint32_t nelem;
-  uint32_t pad;
+  uint32_t first_cell;   // offset / slice elements: the block's first slice-size cell
 };
 struct RingTask {
   uint32_t loop;      // index into the loop table (nranks blocks per loop)

@@ -142,12 +142,29 @@ struct Unit {
   static constexpr int esz = kVecBytes / elems;
 };
 
-// Whole-vector global accesses.  Single-use streams: non-temporal hint.
+// Whole-vector global accesses.  Every byte is read once and written once,
+// so by default both carry the non-temporal (streaming) hint.
+#ifndef EMU_LOAD_NT
+#define EMU_LOAD_NT 1
+#endif
+#ifndef EMU_STORE_NT
+#define EMU_STORE_NT 1
+#endif
 __device__ __forceinline__ u32x4 ld_vec(const void* base, uint64_t byte_off) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off));
+  const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off);
+#if EMU_LOAD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
 }
 __device__ __forceinline__ void st_vec(void* base, uint64_t byte_off, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off));
+  u32x4* p = reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off);
+#if EMU_STORE_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
 }
 
 // Partial vector at the very end of a buffer: `nbytes` (< 16, a multiple of

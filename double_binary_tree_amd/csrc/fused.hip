@@ -19,7 +19,14 @@ namespace emu {
 enum FusedMode : int { kRingFold = 0, kTreeFold = 1, kTreeProgram = 2 };
 
 constexpr int kFusedThreads = 256;
-constexpr int kBatch = 8;   // loads issued back to back before they are folded
+#ifndef EMU_FUSED_VPT
+#define EMU_FUSED_VPT 2
+#endif
+#ifndef EMU_FUSED_BATCH
+#define EMU_FUSED_BATCH 8
+#endif
+constexpr int kVpt = EMU_FUSED_VPT;      // vectors per lane in a full tile
+constexpr int kBatch = EMU_FUSED_BATCH;  // ranks whose loads are issued back to back
 
 // The register stack is indexed with the (wave-uniform) level of the
 // program; the compiler keeps it in VGPRs and indexes it relatively.
@@ -43,91 +50,144 @@ __device__ __forceinline__ uint32_t input_rank(const FusedArgs& a, uint32_t vari
   return a.prog.perm[variant][j];
 }
 
-template <bool FULL>
-__device__ __forceinline__ u32x4 load_input(const void* p, uint64_t boff, int nbytes) {
-  return FULL ? ld_vec(p, boff) : ld_part(p, boff, nbytes);
-}
+// Register stack size: the program mode's stack; the fold modes need none.
+template <int MODE>
+constexpr int stack_regs() { return MODE == kTreeProgram ? kMaxRegs : 1; }
 
-// Fold inputs j .. j+B-1 into the accumulator / register stack.  The B loads
-// are unconditional and issued back to back; the folds then consume them in
-// order.
-template <typename R, int MODE, bool FULL, int B>
-__device__ __forceinline__ void fold_batch(const FusedArgs& a, uint32_t variant, uint32_t j, uint64_t boff,
-                                           int nbytes, u32x4& acc, u32x4 (&g)[kMaxRegs]) {
-  u32x4 x[B];
+template <typename R, int MODE, int V>
+__device__ __forceinline__ void consume(const FusedArgs& a, uint32_t variant, uint32_t j, const u32x4 (&x)[V],
+                                        u32x4 (&acc)[V], u32x4 (&g)[stack_regs<MODE>()]) {
 #pragma unroll
-  for (int i = 0; i < B; ++i) x[i] = load_input<FULL>(a.send[input_rank<MODE>(a, variant, j + i)], boff, nbytes);
-#pragma unroll
-  for (int i = 0; i < B; ++i) {
-    const u32x4 v = R::pre(x[i]);
-    if (MODE == kTreeProgram) {
-      const uint32_t w = a.prog.instr[variant][j + i];
+  for (int v = 0; v < V; ++v) {
+    const u32x4 val = R::pre(x[v]);
+    if constexpr (MODE == kTreeProgram) {
+      const uint32_t w = a.prog.instr[variant][j];
       const int d = (w >> 1) & 7;
-      reg_fold_in<R>(g, d, (w & 1) != 0, v);
+      static_assert(MODE != kTreeProgram || V == 1, "program mode evaluates one position at a time");
+      reg_fold_in<R>(g, d, (w & 1) != 0, val);
       const int pops = (int)(w >> 4);
       for (int p = 1; p <= pops; ++p) reg_fold_down<R>(g, d - p);
     } else {
-      acc = R::op(acc, v);
+      acc[v] = j == 0 ? val : R::op(acc[v], val);
     }
   }
 }
 
-// Evaluate one vector position.  FULL: all 16 bytes valid; otherwise
-// `nbytes` valid bytes (only the very last vector of the message).
-template <typename R, int MODE, bool FULL>
-__device__ __forceinline__ u32x4 evaluate(const FusedArgs& a, uint32_t variant, uint64_t boff,
-                                          int nbytes) {
-  const uint32_t n = a.nranks;
-  u32x4 acc;
-  u32x4 g[kMaxRegs];
-  uint32_t j = 0;
-  if (MODE == kTreeProgram) {
+// Fold inputs j .. j+B-1 at V whole-vector positions (byte offsets boff +
+// v*stride).  The B*V loads are unconditional and issued back to back.
+template <typename R, int MODE, int V, int B>
+__device__ __forceinline__ void fold_batch(const FusedArgs& a, uint32_t variant, uint32_t j, uint64_t boff,
+                                           uint32_t stride, u32x4 (&acc)[V], u32x4 (&g)[stack_regs<MODE>()]) {
+  const void* src[B];
 #pragma unroll
-    for (int i = 0; i < kMaxRegs; ++i) g[i] = u32x4{0, 0, 0, 0};
-    acc = u32x4{0, 0, 0, 0};
-  } else {
-    // the fold starts with its first input as is
-    acc = R::pre(load_input<FULL>(a.send[input_rank<MODE>(a, variant, 0)], boff, nbytes));
-    j = 1;
-  }
-  if (FULL) {
-    for (; j + kBatch <= n; j += kBatch) fold_batch<R, MODE, FULL, kBatch>(a, variant, j, boff, nbytes, acc, g);
-    if (j + 4 <= n) { fold_batch<R, MODE, FULL, 4>(a, variant, j, boff, nbytes, acc, g); j += 4; }
-    if (j + 2 <= n) { fold_batch<R, MODE, FULL, 2>(a, variant, j, boff, nbytes, acc, g); j += 2; }
-  }
-  for (; j < n; ++j) fold_batch<R, MODE, FULL, 1>(a, variant, j, boff, nbytes, acc, g);
-  if (MODE == kTreeProgram) acc = g[0];
-  return R::post(acc);
+  for (int i = 0; i < B; ++i) src[i] = a.send[input_rank<MODE>(a, variant, j + i)];
+  u32x4 x[B][V];
+#pragma unroll
+  for (int i = 0; i < B; ++i)
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[i][v] = ld_vec(src[i], boff + (uint64_t)v * stride);
+  // Keep every load of the batch ahead of the first fold.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < B; ++i) consume<R, MODE, V>(a, variant, j + i, x[i], acc, g);
 }
 
-// Write the result to every rank, stores issued in groups.
-__device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, u32x4 v) {
+// Evaluate V whole-vector positions.
+template <typename R, int MODE, int V>
+__device__ __forceinline__ void evaluate(const FusedArgs& a, uint32_t variant, uint64_t boff, uint32_t stride,
+                                         u32x4 (&out)[V]) {
+  const uint32_t n = a.nranks;
+  u32x4 acc[V];
+  u32x4 g[stack_regs<MODE>()];
+#pragma unroll
+  for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
+  uint32_t j = 0;
+  for (; j + kBatch <= n; j += kBatch) fold_batch<R, MODE, V, kBatch>(a, variant, j, boff, stride, acc, g);
+  if (j + 4 <= n) { fold_batch<R, MODE, V, 4>(a, variant, j, boff, stride, acc, g); j += 4; }
+  if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, variant, j, boff, stride, acc, g); j += 2; }
+  if (j < n) fold_batch<R, MODE, V, 1>(a, variant, j, boff, stride, acc, g);
+#pragma unroll
+  for (int v = 0; v < V; ++v) out[v] = R::post(MODE == kTreeProgram ? g[0] : acc[v]);
+}
+
+// The one partial vector at the end of the message: `nbytes` valid bytes,
+// one rank at a time, 16-bit accesses.
+template <typename R, int MODE>
+__device__ __forceinline__ void partial_vector(const FusedArgs& a, uint32_t variant, uint64_t boff, int nbytes) {
+  u32x4 acc[1];
+  u32x4 g[stack_regs<MODE>()];
+#pragma unroll
+  for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
+  for (uint32_t j = 0; j < a.nranks; ++j) {
+    const u32x4 x[1] = {ld_part(a.send[input_rank<MODE>(a, variant, j)], boff, nbytes)};
+    consume<R, MODE, 1>(a, variant, j, x, acc, g);
+  }
+  const u32x4 res = R::post(MODE == kTreeProgram ? g[0] : acc[0]);
+  for (uint32_t r = 0; r < a.nranks; ++r) st_part(a.recv[r], boff, nbytes, res);
+}
+
+// Write V results to every rank, stores issued in groups.
+template <int V>
+__device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, uint32_t stride, const u32x4 (&res)[V]) {
   const uint32_t n = a.nranks;
   uint32_t r = 0;
   for (; r + kBatch <= n; r += kBatch) {
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) st_vec(a.recv[r + i], boff, v);
+    for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+      for (int v = 0; v < V; ++v) st_vec(a.recv[r + i], boff + (uint64_t)v * stride, res[v]);
   }
-  for (; r < n; ++r) st_vec(a.recv[r], boff, v);
+  for (; r < n; ++r)
+#pragma unroll
+    for (int v = 0; v < V; ++v) st_vec(a.recv[r], boff + (uint64_t)v * stride, res[v]);
 }
 
+// A tile holds kFusedThreads * kVpt vectors; lane l owns vectors l, l + 256,
+// ... (each group of 64 lanes touches 1 KiB contiguous per rank).
+// The tile table comes as its own read-only argument so that the (uniform)
+// descriptor loads go through the scalar unit.
 template <typename R, int MODE, int ESZ>
-__global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs a) {
-  constexpr int unit = kVecBytes / ESZ;
+__global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs a,
+                                                                 const Tile* __restrict__ tiles) {
+  constexpr uint32_t unit = kVecBytes / ESZ;
+  constexpr uint32_t stride = kFusedThreads * kVecBytes;   // bytes between a lane's vectors
   for (uint32_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
-    const Tile tile = a.tiles[t];
-    const uint32_t off = threadIdx.x * unit;
-    if (off >= tile.nelem) continue;
-    const uint32_t left = tile.nelem - off;
-    const uint64_t boff = (tile.start + off) * ESZ;
-    if (left >= (uint32_t)unit) {
-      store_all(a, boff, evaluate<R, MODE, true>(a, tile.variant, boff, kVecBytes));
-    } else {
-      // The one partial vector at the end of the message: one rank at a
-      // time, element-wise accesses.
-      const int nbytes = (int)(left * ESZ);
-      const u32x4 res = evaluate<R, MODE, false>(a, tile.variant, boff, nbytes);
-      for (uint32_t r = 0; r < a.nranks; ++r) st_part(a.recv[r], boff, nbytes, res);
+    const Tile tile = tiles[t];
+    const uint64_t base = tile.start * ESZ;
+    const uint32_t lane_off = threadIdx.x * kVecBytes;
+    if (tile.nelem == kFusedThreads * kVpt * unit) {
+      if (MODE == kTreeProgram) {
+        // The register stack is indexed dynamically; one position at a time
+        // keeps it in VGPRs.
+        for (int v = 0; v < kVpt; ++v) {
+          u32x4 res[1];
+          evaluate<R, MODE, 1>(a, tile.variant, base + lane_off + (uint64_t)v * stride, 0, res);
+          store_all<1>(a, base + lane_off + (uint64_t)v * stride, 0, res);
+        }
+      } else {
+        constexpr int V = MODE == kTreeProgram ? 1 : kVpt;
+        u32x4 res[V];
+        evaluate<R, MODE, V>(a, tile.variant, base + lane_off, stride, res);
+        store_all<V>(a, base + lane_off, stride, res);
+      }
+      continue;
+    }
+    // A short tile (next to a segment boundary): vector by vector, each lane
+    // keeping its position in the aligned tile-size cell, so that the wave
+    // still touches whole cache lines; lanes outside the tile sit out.
+    const uint64_t cell = tile.start / (kFusedThreads * kVpt * unit) * (kFusedThreads * kVpt * unit);
+    const uint64_t end = tile.start + tile.nelem;
+    for (int v = 0; v < kVpt; ++v) {
+      const uint64_t pos = cell + (uint64_t)(threadIdx.x + v * kFusedThreads) * unit;
+      if (pos < tile.start || pos >= end) continue;
+      const uint64_t boff = pos * ESZ;
+      if (end - pos >= unit) {
+        u32x4 res[1];
+        evaluate<R, MODE, 1>(a, tile.variant, boff, 0, res);
+        store_all<1>(a, boff, 0, res);
+      } else {
+        partial_vector<R, MODE>(a, tile.variant, boff, (int)((end - pos) * ESZ));
+      }
     }
   }
 }
@@ -135,7 +195,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs
 template <DType T, Op O, int MODE>
 static hipError_t launch_one(const FusedArgs& a, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((fused_allreduce<Red<T, O>, MODE, Unit<T>::esz>), dim3(grid), dim3(kFusedThreads),
-                     0, stream, a);
+                     0, stream, a, a.tiles);
   return hipGetLastError();
 }
 
@@ -165,6 +225,6 @@ hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, int grid, 
   return hipErrorInvalidValue;
 }
 
-int fused_threads() { return kFusedThreads; }
+int fused_tile_vectors() { return kFusedThreads * kVpt; }
 
 }  // namespace emu

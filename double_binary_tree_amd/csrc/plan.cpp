@@ -80,10 +80,20 @@ void build_fused_tiles(const Topology& topo, Algo algo, uint64_t count, uint64_t
       push(chans[c].offset, chans[c].count, (uint32_t)topo.channels[c].tree_index);
     }
   }
+  // Cut at global multiples of the tile size, so that full tiles start on a
+  // tile-size (>= 4 KiB) boundary of every rank buffer and each wave's
+  // accesses cover whole cache lines; only the pieces next to a segment
+  // boundary are short.
   out->clear();
-  for (const Seg& s : segs)
-    for (uint64_t e = 0; e < s.len; e += tile_elems)
-      out->push_back({s.start + e, (uint32_t)std::min(tile_elems, s.len - e), s.variant});
+  for (const Seg& s : segs) {
+    uint64_t pos = s.start;
+    const uint64_t end = s.start + s.len;
+    while (pos < end) {
+      const uint64_t next = std::min(end, (pos / tile_elems + 1) * tile_elems);
+      out->push_back({pos, (uint32_t)(next - pos), s.variant});
+      pos = next;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -219,12 +229,13 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
   uint32_t loop_id = 0;
   for (const Range& ch : channel_ranges(count, unit, topo.nchannels)) {
     for (const auto& blocks : ring_loops(ch, topo.nranks, chunk_count, unit)) {
-      uint64_t longest = 0;
+      // slices of a block = the slice-size cells of the global grid it overlaps
+      uint64_t nslices = 0;
       for (const Range& b : blocks) {
-        loops->push_back({b.offset, (uint32_t)b.count, 0});
-        longest = std::max(longest, b.count);
+        loops->push_back({b.offset, (uint32_t)b.count, (uint32_t)(b.offset / slice_elems)});
+        if (b.count)
+          nslices = std::max(nslices, ceil_div(b.offset + b.count, slice_elems) - b.offset / slice_elems);
       }
-      const uint64_t nslices = ceil_div(longest, slice_elems);
       for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q});
       ++loop_id;
     }
@@ -236,10 +247,18 @@ void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
                       std::vector<TreeNode>* nodes) {
   tasks->clear();
   const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
+  // Tasks stay inside one chunk and are cut at global multiples of
+  // task_elems, so every task after a chunk's first starts aligned.
   for (int c = 0; c < topo.nchannels; ++c)
-    for (const Range& ck : tree_chunks(chans[c], chunk_count))
-      for (uint64_t e = 0; e < ck.count; e += task_elems)
-        tasks->push_back({ck.offset + e, (uint32_t)std::min(task_elems, ck.count - e), (uint32_t)c});
+    for (const Range& ck : tree_chunks(chans[c], chunk_count)) {
+      uint64_t pos = ck.offset;
+      const uint64_t end = ck.offset + ck.count;
+      while (pos < end) {
+        const uint64_t next = std::min(end, (pos / task_elems + 1) * task_elems);
+        tasks->push_back({pos, (uint32_t)(next - pos), (uint32_t)c});
+        pos = next;
+      }
+    }
   nodes->assign((size_t)topo.nchannels * topo.nranks, TreeNode{});
   for (int c = 0; c < topo.nchannels; ++c)
     for (int r = 0; r < topo.nranks; ++r) {

@@ -35,69 +35,110 @@ __device__ __forceinline__ void step_barrier() {
 
 // ---------------------------------------------------------------------------
 // Ring.
+// Vectors per lane per step and how many steps of a rank's own input are
+// loaded ahead.  Larger values keep more bytes in flight per wave but cost
+// registers (and so resident workgroups); these are the measured optima for
+// each kernel on MI355X.
+#ifndef EMU_RING_VPT
+#define EMU_RING_VPT 2
+#endif
+#ifndef EMU_RING_PREFETCH
+#define EMU_RING_PREFETCH 1
+#endif
+#ifndef EMU_TREE_VPT
+#define EMU_TREE_VPT 1
+#endif
+#ifndef EMU_TREE_PREFETCH
+#define EMU_TREE_PREFETCH 3
+#endif
+
 template <typename R, int ESZ>
 __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   constexpr int unit = kVecBytes / ESZ;
-  extern __shared__ u32x4 fifo[];   // [2][N][G]
+  constexpr int V = EMU_RING_VPT;
+  constexpr int kPrefetch = EMU_RING_PREFETCH;
+  extern __shared__ u32x4 fifo[];   // [2][N][V][G]
   const uint32_t n = a.nranks, g = a.group;
   const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;
   const bool active = r < n;
   const uint32_t prev = active ? (r + n - 1) % n : 0;
   const RingLoopBlock* loops = static_cast<const RingLoopBlock*>(a.table);
   const RingTask* tasks = static_cast<const RingTask*>(a.tasks);
-  auto slot = [&](uint32_t parity, uint32_t rank) -> u32x4& { return fifo[(parity * n + rank) * g + p]; };
+  auto slot = [&](uint32_t parity, uint32_t rank, int v) -> u32x4& {
+    return fifo[((parity * n + rank) * V + v) * g + p];
+  };
 
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x) {
     const RingTask task = tasks[t];
     const RingLoopBlock* blk = loops + (size_t)task.loop * n;
-    const uint64_t in_block = ((uint64_t)task.slice * g + p) * unit;   // element offset inside a block
-    // bytes of block b this lane owns (0 if the block is shorter)
-    auto nbytes_of = [&](uint32_t b) -> int {
-      const uint64_t len = blk[b].nelem;
-      if (in_block >= len) return 0;
-      const uint64_t left = len - in_block;
+    // Slice q of block b is the q-th slice-size cell of the global element
+    // grid that the block overlaps; lane p's vector v sits at a fixed place in
+    // the cell (aligned accesses), and is live only inside the block.
+    const uint64_t slice_elems = (uint64_t)V * g * unit;
+    auto pos_of = [&](uint32_t b, int v) -> uint64_t {
+      return ((uint64_t)blk[b].first_cell + task.slice) * slice_elems + ((uint64_t)v * g + p) * unit;
+    };
+    auto nbytes_of = [&](uint32_t b, int v) -> int {
+      const uint64_t pos = pos_of(b, v), start = blk[b].offset, end = start + blk[b].nelem;
+      if (pos < start || pos >= end) return 0;
+      const uint64_t left = end - pos;
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
-    auto boff_of = [&](uint32_t b) -> uint64_t { return (blk[b].offset + in_block) * ESZ; };
+    auto boff_of = [&](uint32_t b, int v) -> uint64_t { return pos_of(b, v) * ESZ; };
+    auto load_block = [&](uint32_t b, u32x4 (&x)[V]) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int nb = nbytes_of(b, v);
+        x[v] = nb ? ld_any(a.send[r], boff_of(b, v), nb) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int nb = nbytes_of(b, v);
+        if (nb) st_any(a.recv[r], boff_of(b, v), nb, R::post(x[v]));
+      }
+    };
 
     if (n == 1) {
-      const int nb = nbytes_of(0);
-      if (active && nb) st_any(a.recv[0], boff_of(0), nb, ld_any(a.send[0], boff_of(0), nb));
+      if (active) {
+        u32x4 x[V];
+        load_block(0, x);
+        store_block(0, x);
+      }
       continue;
     }
-    // step 0: send own block r
-    u32x4 own = {0, 0, 0, 0};
+    // step 0: send own block r; the blocks of steps 1..PF are loaded ahead
+    // (queue q[0] is the next step's block).
+    u32x4 own[V], q[kPrefetch][V];
     if (active) {
-      const int nb = nbytes_of(r);
-      if (nb) own = ld_any(a.send[r], boff_of(r), nb);
+      load_block(r, own);
+#pragma unroll
+      for (int i = 0; i < kPrefetch; ++i)
+        if ((uint32_t)i + 1 < n) load_block((r + 2 * n - 1 - i) % n, q[i]);
+#pragma unroll
+      for (int v = 0; v < V; ++v) slot(0, r, v) = R::pre(own[v]);
     }
-    // prefetch the block of step 1
-    u32x4 next = {0, 0, 0, 0};
-    if (active) {
-      const uint32_t b1 = (r + n - 1) % n;
-      const int nb = nbytes_of(b1);
-      if (nb) next = ld_any(a.send[r], boff_of(b1), nb);
-    }
-    if (active) slot(0, r) = R::pre(own);
     step_barrier();
 
     // reduce-scatter steps 1..N-1
     for (uint32_t s = 1; s < n; ++s) {
       const uint32_t b = (r + n - s) % n;
-      u32x4 mine = next;
-      if (active && s + 1 < n) {
-        const uint32_t bn = (r + n - s - 1) % n;
-        const int nb = nbytes_of(bn);
-        if (nb) next = ld_any(a.send[r], boff_of(bn), nb);
-      }
       if (active) {
-        const u32x4 incoming = slot((s - 1) & 1, prev);
-        const u32x4 res = R::op(R::pre(mine), incoming);
-        if (s == n - 1) {
-          const int nb = nbytes_of(b);
-          if (nb) st_any(a.recv[r], boff_of(b), nb, R::post(res));
-        }
-        slot(s & 1, r) = res;
+        u32x4 mine[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) mine[v] = q[0][v];
+#pragma unroll
+        for (int i = 0; i + 1 < kPrefetch; ++i)
+#pragma unroll
+          for (int v = 0; v < V; ++v) q[i][v] = q[i + 1][v];
+        if (s + kPrefetch < n) load_block((r + 2 * n - s - kPrefetch) % n, q[kPrefetch - 1]);
+        u32x4 res[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) res[v] = R::op(R::pre(mine[v]), slot((s - 1) & 1, prev, v));
+        if (s == n - 1) store_block(b, res);
+#pragma unroll
+        for (int v = 0; v < V; ++v) slot(s & 1, r, v) = res[v];
       }
       step_barrier();
     }
@@ -105,10 +146,14 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
     for (uint32_t j = 1; j < n; ++j) {
       const uint32_t b = (r + 1 + n - j) % n;
       if (active) {
-        const u32x4 v = slot((n - 2 + j) & 1, prev);
-        const int nb = nbytes_of(b);
-        if (nb) st_any(a.recv[r], boff_of(b), nb, R::post(v));
-        if (j + 1 < n) slot((n - 1 + j) & 1, r) = v;
+        u32x4 x[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = slot((n - 2 + j) & 1, prev, v);
+        store_block(b, x);
+        if (j + 1 < n) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) slot((n - 1 + j) & 1, r, v) = x[v];
+        }
       }
       step_barrier();
     }
@@ -120,17 +165,21 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
 template <typename R, int ESZ>
 __global__ __launch_bounds__(1024) void step_tree(const StepArgs a) {
   constexpr int unit = kVecBytes / ESZ;
-  extern __shared__ u32x4 fifo[];   // up[2][N][G] then down[2][N][G]
+  constexpr int V = EMU_TREE_VPT;
+  constexpr int kPrefetch = EMU_TREE_PREFETCH;
+  extern __shared__ u32x4 fifo[];   // up[2][N][V][G] then down[2][N][V][G]
   const uint32_t n = a.nranks, g = a.group;
   const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;
   const bool active = r < n;
   const TreeTask* tasks = static_cast<const TreeTask*>(a.tasks);
   const TreeNode* nodes = static_cast<const TreeNode*>(a.table);
   const int H = (int)a.height;
-  const uint32_t slice_elems = g * unit;
-  auto up_slot = [&](int parity, uint32_t rank) -> u32x4& { return fifo[((uint32_t)parity * n + rank) * g + p]; };
-  auto dn_slot = [&](int parity, uint32_t rank) -> u32x4& {
-    return fifo[((2u + (uint32_t)parity) * n + rank) * g + p];
+  const uint32_t slice_elems = V * g * unit;
+  auto up_slot = [&](int parity, uint32_t rank, int v) -> u32x4& {
+    return fifo[(((uint32_t)parity * n + rank) * V + v) * g + p];
+  };
+  auto dn_slot = [&](int parity, uint32_t rank, int v) -> u32x4& {
+    return fifo[(((2u + (uint32_t)parity) * n + rank) * V + v) * g + p];
   };
 
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x) {
@@ -139,67 +188,111 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a) {
     const int depth = me.depth;
     const bool is_root = me.up < 0;
     const bool has_children = me.down[0] >= 0;
-    const int nslices = (int)((task.nelem + slice_elems - 1) / slice_elems);
-    auto nbytes_of = [&](int q) -> int {
-      const uint64_t off = (uint64_t)q * slice_elems + (uint64_t)p * unit;
-      if (off >= task.nelem) return 0;
-      const uint64_t left = task.nelem - off;
+    // Slices are the slice-size cells of the global element grid that the
+    // task overlaps; lanes outside [start, start + nelem) sit out.
+    const uint64_t first_cell = task.start / slice_elems;
+    const uint64_t end = task.start + task.nelem;
+    const int nslices = (int)((end + slice_elems - 1) / slice_elems - first_cell);
+    auto pos_of = [&](int q, int v) -> uint64_t {
+      return (first_cell + (uint64_t)q) * slice_elems + ((uint64_t)v * g + p) * unit;
+    };
+    auto nbytes_of = [&](int q, int v) -> int {
+      const uint64_t pos = pos_of(q, v);
+      if (pos < task.start || pos >= end) return 0;
+      const uint64_t left = end - pos;
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
-    auto boff_of = [&](int q) -> uint64_t {
-      return (task.start + (uint64_t)q * slice_elems + (uint64_t)p * unit) * ESZ;
+    auto boff_of = [&](int q, int v) -> uint64_t { return pos_of(q, v) * ESZ; };
+    auto load_slice = [&](int q, u32x4 (&x)[V]) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int nb = nbytes_of(q, v);
+        x[v] = nb ? ld_any(a.send[r], boff_of(q, v), nb) : u32x4{0, 0, 0, 0};
+      }
+    };
+    auto store_slice = [&](int q, const u32x4 (&x)[V]) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int nb = nbytes_of(q, v);
+        if (nb) st_any(a.recv[r], boff_of(q, v), nb, R::post(x[v]));
+      }
     };
     const int up_lag = H - depth;        // reduce slice q at stage q + up_lag
     const int dn_lag = H + depth;        // broadcast slice q at stage q + dn_lag
     const int nstages = nslices + 2 * H;
 
-    // prefetch own input of the first reduce slice
-    u32x4 next = {0, 0, 0, 0};
-    if (active && nslices > 0) {
-      const int nb = nbytes_of(0);
-      if (nb) next = ld_any(a.send[r], boff_of(0), nb);
+    // own inputs of the next kPrefetch reduce slices are loaded ahead
+    // (queue q[0] is the next one).
+    u32x4 q[kPrefetch][V];
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < kPrefetch; ++i)
+        if (i < nslices) load_slice(i, q[i]);
     }
     for (int st = 0; st < nstages; ++st) {
       const int cur = st & 1, prv = cur ^ 1;
       const int qu = st - up_lag;
       if (active && qu >= 0 && qu < nslices) {
-        u32x4 acc = R::pre(next);
-        if (qu + 1 < nslices) {
-          const int nb = nbytes_of(qu + 1);
-          if (nb) next = ld_any(a.send[r], boff_of(qu + 1), nb);
-        }
+        u32x4 acc[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = R::pre(q[0][v]);
+#pragma unroll
+        for (int i = 0; i + 1 < kPrefetch; ++i)
+#pragma unroll
+          for (int v = 0; v < V; ++v) q[i][v] = q[i + 1][v];
+        if (qu + kPrefetch < nslices) load_slice(qu + kPrefetch, q[kPrefetch - 1]);
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
           const int c = me.down[s];
-          if (c >= 0) acc = R::op(acc, up_slot(prv, (uint32_t)c));
+          if (c >= 0) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) acc[v] = R::op(acc[v], up_slot(prv, (uint32_t)c, v));
+          }
         }
         if (is_root) {
-          const int nb = nbytes_of(qu);
-          if (nb) st_any(a.recv[r], boff_of(qu), nb, R::post(acc));
-          if (has_children) dn_slot(cur, r) = acc;
+          store_slice(qu, acc);
+          if (has_children) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) dn_slot(cur, r, v) = acc[v];
+          }
         } else {
-          up_slot(cur, r) = acc;
+#pragma unroll
+          for (int v = 0; v < V; ++v) up_slot(cur, r, v) = acc[v];
         }
       }
       const int qd = st - dn_lag;
       if (active && !is_root && qd >= 0 && qd < nslices) {
-        const u32x4 v = dn_slot(prv, (uint32_t)me.up);
-        const int nb = nbytes_of(qd);
-        if (nb) st_any(a.recv[r], boff_of(qd), nb, R::post(v));
-        if (has_children) dn_slot(cur, r) = v;
+        u32x4 x[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) x[v] = dn_slot(prv, (uint32_t)me.up, v);
+        store_slice(qd, x);
+        if (has_children) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) dn_slot(cur, r, v) = x[v];
+        }
       }
       step_barrier();
     }
   }
 }
 
+// Kernels that use more than 64 KiB of dynamic LDS must say so before launch.
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
+}
+
 template <DType T, Op O>
 static hipError_t launch_ring_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
+  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz>, lds)) return e;
   hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz>), dim3(grid), dim3(block), lds, s, a);
   return hipGetLastError();
 }
 template <DType T, Op O>
 static hipError_t launch_tree_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
+  if (hipError_t e = allow_lds(step_tree<Red<T, O>, Unit<T>::esz>, lds)) return e;
   hipLaunchKernelGGL((step_tree<Red<T, O>, Unit<T>::esz>), dim3(grid), dim3(block), lds, s, a);
   return hipGetLastError();
 }
@@ -225,6 +318,8 @@ hipError_t launch_stepwise(bool ring, DType t, Op op, const StepArgs& a, int gri
   }
   return hipErrorInvalidValue;
 }
+
+int stepwise_vectors_per_lane(bool ring) { return ring ? EMU_RING_VPT : EMU_TREE_VPT; }
 
 // Resident workgroups per CU for the stepwise kernels at this block/LDS size.
 int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds) {

@@ -10,7 +10,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libemucomm.so")
+# EMUCOMM_LIB may point at another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is used.
+LIB_PATH = os.environ.get("EMUCOMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                         "libemucomm.so")
 
 ALGO = {"ring": 0, "tree": 1}
 MODE = {"stepwise": 0x000, "fused": 0x100}

@@ -82,10 +82,14 @@ extern "C" {
  *               the first ceil(nchannels/2) channels use tree 0, the others
  *               tree 1 (the duplicated channel records of section "节点内先
  *               形成链").
- *   chunk_bytes > 0, a multiple of 16.  Tree: chunk size inside a channel;
- *               ring: each loop covers nranks chunks.
+ *   chunk_bytes > 0, a multiple of 16, at most 1 GiB.  Tree: chunk size
+ *               inside a channel; ring: each loop covers nranks chunks.
  * Host only: touches no GPU (device resources are created on the first
- * emu_allreduce).  Replaces any previous communicator.
+ * emu_allreduce), except that when more than 16 configurations have been
+ * initialised in the process the cached ones are dropped, which waits for
+ * the device to go idle before freeing their tables.  Replaces any previous
+ * communicator; re-initialising with arguments used before reuses the
+ * tables built for them.
  * Errors: EMU_ERR_INVALID_ARGUMENT for out-of-range arguments (state left
  * unchanged); EMU_ERR_INTERNAL if a tree record overflows (cannot happen
  * within the limits above).
@@ -108,6 +112,7 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
  * read during the call only; the device buffers must stay alive until the
  * stream work completes.  The caller owns all buffers and the stream; the
  * library owns its tables and device workspace.
+ * count * element size must not exceed 2^40 bytes.
  * Errors (checked before anything is enqueued): EMU_ERR_NOT_INITIALIZED,
  * EMU_ERR_INVALID_ARGUMENT; EMU_ERR_HIP when the runtime refuses an
  * allocation, copy or launch.  Faults inside kernels surface at the stream

@@ -75,7 +75,7 @@ def test_init_rejects_bad_arguments_and_keeps_state():
     E.comm_init(4, 2, "tree", 2, 1 << 19)
     bad = [
         (0, 1, 1, 1, 1 << 19), (65, 1, 1, 1, 1 << 19), (4, 3, 1, 1, 1 << 19), (4, 0, 1, 1, 1 << 19),
-        (4, 1, 1, 0, 1 << 19), (4, 1, 1, 65, 1 << 19), (4, 1, 1, 1, 0), (4, 1, 1, 1, 24),
+        (4, 1, 1, 0, 1 << 19), (4, 1, 1, 65, 1 << 19), (4, 1, 1, 1, 0), (4, 1, 1, 1, 24), (4, 1, 1, 1, (1 << 30) + 16),
         (4, 1, 7, 1, 1 << 19), (4, 1, 0x201, 1, 1 << 19),
     ]
     for args in bad:

@@ -112,7 +112,7 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
     build_fused_tiles(c.topo, c.algo, count, unit, chunk_count, tile_elems, &tiles);
     p->ntiles = (uint32_t)tiles.size();
     if (int e = p->tiles.upload(tiles.data(), tiles.size() * sizeof(Tile))) return e;
-    const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 32);
+    const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 64);
     p->fused_grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntiles, (uint64_t)cus * per_cu));
     return EMU_SUCCESS;
   }
@@ -122,7 +122,8 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   // Lanes per virtual rank: the widest group that fits one workgroup
   // (N*G <= 1024 threads) and the device's LDS per workgroup.
   const size_t lds_limit = lds_per_block(dev);
-  p->group = 64;
+  p->group = (int)env_long("EMU_STEP_GROUP", 64);   // tuning override; must be a power of two
+  if (p->group > 64 || (p->group & (p->group - 1))) p->group = 64;
   auto lds_of = [&](int g) { return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes; };
   while (p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
   if (n * p->group > 1024 || lds_of(p->group) > lds_limit) return EMU_ERR_INTERNAL;

@@ -20,7 +20,7 @@ enum FusedMode : int { kRingFold = 0, kTreeFold = 1, kTreeProgram = 2 };
 
 constexpr int kFusedThreads = 256;
 #ifndef EMU_FUSED_VPT
-#define EMU_FUSED_VPT 2
+#define EMU_FUSED_VPT 1
 #endif
 #ifndef EMU_FUSED_BATCH
 #define EMU_FUSED_BATCH 8
@@ -87,7 +87,12 @@ __device__ __forceinline__ void fold_batch(const FusedArgs& a, uint32_t variant,
 #pragma unroll
     for (int v = 0; v < V; ++v) x[i][v] = ld_vec(src[i], boff + (uint64_t)v * stride);
   // Keep every load of the batch ahead of the first fold.
+#ifndef EMU_SCHED_BARRIER
+#define EMU_SCHED_BARRIER 1
+#endif
+#if EMU_SCHED_BARRIER
   __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
   for (int i = 0; i < B; ++i) consume<R, MODE, V>(a, variant, j + i, x[i], acc, g);
 }
@@ -126,17 +131,22 @@ __device__ __forceinline__ void partial_vector(const FusedArgs& a, uint32_t vari
   for (uint32_t r = 0; r < a.nranks; ++r) st_part(a.recv[r], boff, nbytes, res);
 }
 
-// Write V results to every rank, stores issued in groups.
+// Write V results to every rank.
+#ifndef EMU_STORE_GROUPS
+#define EMU_STORE_GROUPS 0
+#endif
 template <int V>
 __device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, uint32_t stride, const u32x4 (&res)[V]) {
   const uint32_t n = a.nranks;
   uint32_t r = 0;
+#if EMU_STORE_GROUPS
   for (; r + kBatch <= n; r += kBatch) {
 #pragma unroll
     for (int i = 0; i < kBatch; ++i)
 #pragma unroll
       for (int v = 0; v < V; ++v) st_vec(a.recv[r + i], boff + (uint64_t)v * stride, res[v]);
   }
+#endif
   for (; r < n; ++r)
 #pragma unroll
     for (int v = 0; v < V; ++v) st_vec(a.recv[r], boff + (uint64_t)v * stride, res[v]);

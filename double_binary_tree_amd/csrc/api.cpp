@@ -58,7 +58,7 @@ struct Plan {
   uint32_t ntasks = 0;
   int group = 0, block = 0, grid = 0;
   size_t lds = 0;
-  uint32_t nslices = 0, height = 0;
+  uint32_t height = 0;
 };
 
 struct Comm {
@@ -124,7 +124,11 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   const size_t lds_limit = lds_per_block(dev);
   p->group = (int)env_long("EMU_STEP_GROUP", 64);   // tuning override; must be a power of two
   if (p->group > 64 || (p->group & (p->group - 1))) p->group = 64;
-  auto lds_of = [&](int g) { return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes; };
+  // LDS: ring 2 parities of slots plus 2 x N staged block descriptors, tree
+  // 2 parities x (up, down) slots.
+  auto lds_of = [&](int g) {
+    return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes + (ring ? 2u * n * sizeof(RingLoopBlock) : 0u);
+  };
   while (p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
   if (n * p->group > 1024 || lds_of(p->group) > lds_limit) return EMU_ERR_INTERNAL;
   p->block = (n * p->group + 63) / 64 * 64;
@@ -139,10 +143,13 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
     if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
   } else {
-    p->nslices = (uint32_t)env_long("EMU_TREE_SLICES", 32);
+    // One pipeline per resident workgroup (tasks per CU = occupancy, or the
+    // tuning override EMU_TREE_TASKS_PER_CU).
+    const int occ_t = stepwise_occupancy(false, t, op, p->block, p->lds);
+    const long per_cu = env_long("EMU_TREE_TASKS_PER_CU", occ_t);
     std::vector<TreeTask> tasks;
     std::vector<TreeNode> nodes;
-    build_tree_tasks(c.topo, count, unit, chunk_count, p->nslices * slice_elems, &tasks, &nodes);
+    build_tree_tasks(c.topo, count, unit, slice_elems, (uint64_t)cus * per_cu, &tasks, &nodes);
     p->ntasks = (uint32_t)tasks.size();
     uint32_t h = 0;
     for (const auto& ch : c.topo.channels) h = std::max<uint32_t>(h, (uint32_t)ch.height);
@@ -279,7 +286,6 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
     a.ntasks = p.ntasks;
     a.nranks = (uint32_t)n;
     a.group = (uint32_t)p.group;
-    a.nslices = p.nslices;
     a.height = p.height;
     err = launch_stepwise(c->algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
   }

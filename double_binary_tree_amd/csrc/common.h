@@ -70,12 +70,12 @@ struct RingTask {
   uint32_t slice;     // slice index inside each block
 };
 
-// Stepwise tree: one task = a run of consecutive slices inside one chunk of
-// one channel.
+// Stepwise tree: one task = a run of consecutive slices of the message that
+// all use one node-level tree.
 struct TreeTask {
   uint64_t start;     // first element
-  uint32_t nelem;     // elements covered (<= nslices * slice elements)
-  uint32_t channel;
+  uint32_t nelem;     // elements covered
+  uint32_t channel;   // a channel of the task's node-level tree
 };
 // Tree record of one rank in one channel, plus its distance from the root.
 struct TreeNode {
@@ -95,7 +95,6 @@ struct StepArgs {
   uint32_t ntasks;
   uint32_t nranks;
   uint32_t group;             // lanes per virtual rank
-  uint32_t nslices;           // tree: slices per task
   uint32_t height;            // tree: max depth over the channel trees
 };
 

@@ -242,23 +242,42 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
   }
 }
 
-void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,
-                      uint64_t task_elems, std::vector<TreeTask>* tasks,
+void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t slice_elems,
+                      uint64_t target_tasks, std::vector<TreeTask>* tasks,
                       std::vector<TreeNode>* nodes) {
   tasks->clear();
   const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
-  // Tasks stay inside one chunk and are cut at global multiples of
-  // task_elems, so every task after a chunk's first starts aligned.
-  for (int c = 0; c < topo.nchannels; ++c)
-    for (const Range& ck : tree_chunks(chans[c], chunk_count)) {
-      uint64_t pos = ck.offset;
-      const uint64_t end = ck.offset + ck.count;
-      while (pos < end) {
-        const uint64_t next = std::min(end, (pos / task_elems + 1) * task_elems);
-        tasks->push_back({pos, (uint32_t)(next - pos), (uint32_t)c});
-        pos = next;
-      }
+  // Channels that use the same node-level tree are contiguous ranges of the
+  // message with identical per-element orders; each such segment is one
+  // stream of slices.  It is cut, at slice-cell boundaries, into pieces of
+  // nearly equal size, one pipeline per workgroup, so that the pipeline's
+  // fill and drain are paid once per piece rather than once per chunk
+  // (chunking never changes an element's order).
+  struct Seg { uint64_t start, end; int channel; };
+  std::vector<Seg> segs;
+  for (int c = 0; c < topo.nchannels; ++c) {
+    if (chans[c].count == 0) continue;
+    if (!segs.empty() && topo.channels[segs.back().channel].tree_index == topo.channels[c].tree_index &&
+        segs.back().end == chans[c].offset)
+      segs.back().end = chans[c].offset + chans[c].count;
+    else
+      segs.push_back({chans[c].offset, chans[c].offset + chans[c].count, c});
+  }
+  uint64_t total_cells = 0;
+  for (const Seg& g : segs) total_cells += ceil_div(g.end, slice_elems) - g.start / slice_elems;
+  if (target_tasks == 0) target_tasks = 1;
+  // Cells per task: even split of all cells, and few enough elements that a
+  // task's length fits the 32-bit field.
+  uint64_t per_task = std::max<uint64_t>(1, ceil_div(total_cells, target_tasks));
+  per_task = std::min<uint64_t>(per_task, ((uint64_t)1 << 31) / slice_elems);
+  for (const Seg& g : segs) {
+    uint64_t pos = g.start;
+    while (pos < g.end) {
+      const uint64_t next = std::min(g.end, (pos / slice_elems + per_task) * slice_elems);
+      tasks->push_back({pos, (uint32_t)(next - pos), (uint32_t)g.channel});
+      pos = next;
     }
+  }
   nodes->assign((size_t)topo.nchannels * topo.nranks, TreeNode{});
   for (int c = 0; c < topo.nchannels; ++c)
     for (int r = 0; r < topo.nranks; ++r) {

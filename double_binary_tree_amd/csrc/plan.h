@@ -41,10 +41,11 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
                       uint64_t slice_elems, std::vector<RingLoopBlock>* loops,
                       std::vector<RingTask>* tasks);
 
-// Stepwise tree: tasks of at most nslices*slice_elems elements inside one
-// chunk of one channel, and the per-(channel, rank) tree table.
-void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,
-                      uint64_t task_elems, std::vector<TreeTask>* tasks,
+// Stepwise tree: about target_tasks contiguous pieces of the message, each
+// inside one run of channels that share a node-level tree and cut at
+// slice-cell boundaries, and the per-(channel, rank) tree table.
+void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t slice_elems,
+                      uint64_t target_tasks, std::vector<TreeTask>* tasks,
                       std::vector<TreeNode>* nodes);
 
 }  // namespace emu

@@ -36,7 +36,7 @@ __device__ __forceinline__ void step_barrier() {
 // ---------------------------------------------------------------------------
 // Ring.
 // Vectors per lane per step and how many steps of a rank's own input are
-// loaded ahead.  Larger values keep more bytes in flight per wave but cost
+// loaded ahead (the ring loads one step ahead).  Larger values keep more bytes in flight per wave but cost
 // registers (and so resident workgroups); these are the measured optima for
 // each kernel on MI355X.
 #ifndef EMU_RING_VPT
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_RING_VPT;
   constexpr int kPrefetch = EMU_RING_PREFETCH;
-  extern __shared__ u32x4 fifo[];   // [2][N][V][G]
+  extern __shared__ u32x4 fifo[];   // slots [2][N][V][G], then descriptors [2][N]
   const uint32_t n = a.nranks, g = a.group;
   const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;
   const bool active = r < n;
@@ -67,10 +67,22 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   auto slot = [&](uint32_t parity, uint32_t rank, int v) -> u32x4& {
     return fifo[((parity * n + rank) * V + v) * g + p];
   };
+  // Block descriptors of the current and the next task, staged in LDS (two
+  // sets) so that no step waits on a descriptor load: the next task's are
+  // copied during the current task's first step.
+  RingLoopBlock* desc = reinterpret_cast<RingLoopBlock*>(fifo + 2 * (size_t)n * V * g);   // [2][N]
+  auto stage_desc = [&](uint32_t t, uint32_t set) {
+    if (t < a.ntasks && threadIdx.x < n)
+      desc[set * n + threadIdx.x] = loops[(size_t)tasks[t].loop * n + threadIdx.x];
+  };
+  stage_desc(blockIdx.x, 0);
+  step_barrier();
 
-  for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x) {
+  uint32_t set = 0;
+  for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x, set ^= 1) {
     const RingTask task = tasks[t];
-    const RingLoopBlock* blk = loops + (size_t)task.loop * n;
+    const RingLoopBlock* blk = desc + set * n;
+    if (n > 1) stage_desc(t + gridDim.x, set ^ 1);   // visible after this task's barriers
     // Slice q of block b is the q-th slice-size cell of the global element
     // grid that the block overlaps; lane p's vector v sits at a fixed place in
     // the cell (aligned accesses), and is live only inside the block.
@@ -106,6 +118,10 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
         load_block(0, x);
         store_block(0, x);
       }
+      // one rank: no steps, so stage the next descriptor here
+      step_barrier();
+      stage_desc(t + gridDim.x, set ^ 1);
+      step_barrier();
       continue;
     }
     // step 0: send own block r; the blocks of steps 1..PF are loaded ahead

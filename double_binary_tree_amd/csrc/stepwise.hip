@@ -36,20 +36,20 @@ __device__ __forceinline__ void step_barrier() {
 // ---------------------------------------------------------------------------
 // Ring.
 // Vectors per lane per step and how many steps of a rank's own input are
-// loaded ahead (the ring loads one step ahead).  Larger values keep more bytes in flight per wave but cost
+// loaded ahead.  Larger values keep more bytes in flight per wave but cost
 // registers (and so resident workgroups); these are the measured optima for
 // each kernel on MI355X.
 #ifndef EMU_RING_VPT
-#define EMU_RING_VPT 2
+#define EMU_RING_VPT 1
 #endif
 #ifndef EMU_RING_PREFETCH
-#define EMU_RING_PREFETCH 1
+#define EMU_RING_PREFETCH 2
 #endif
 #ifndef EMU_TREE_VPT
 #define EMU_TREE_VPT 1
 #endif
 #ifndef EMU_TREE_PREFETCH
-#define EMU_TREE_PREFETCH 3
+#define EMU_TREE_PREFETCH 1
 #endif
 
 template <typename R, int ESZ>

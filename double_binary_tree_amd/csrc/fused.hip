@@ -18,7 +18,10 @@ namespace emu {
 
 enum FusedMode : int { kRingFold = 0, kTreeFold = 1, kTreeProgram = 2 };
 
-constexpr int kFusedThreads = 256;
+#ifndef EMU_FUSED_THREADS
+#define EMU_FUSED_THREADS 256
+#endif
+constexpr int kFusedThreads = EMU_FUSED_THREADS;
 #ifndef EMU_FUSED_VPT
 #define EMU_FUSED_VPT 1
 #endif
@@ -27,6 +30,7 @@ constexpr int kFusedThreads = 256;
 #endif
 constexpr int kVpt = EMU_FUSED_VPT;      // vectors per lane in a full tile
 constexpr int kBatch = EMU_FUSED_BATCH;  // ranks whose loads are issued back to back
+static_assert(kBatch >= 4, "the remainder of a batch is folded 4, 2 and 1 inputs at a time");
 
 // The register stack is indexed with the (wave-uniform) level of the
 // program; the compiler keeps it in VGPRs and indexes it relatively.
@@ -108,7 +112,7 @@ __device__ __forceinline__ void evaluate(const FusedArgs& a, uint32_t variant, u
   for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
   uint32_t j = 0;
   for (; j + kBatch <= n; j += kBatch) fold_batch<R, MODE, V, kBatch>(a, variant, j, boff, stride, acc, g);
-  if (j + 4 <= n) { fold_batch<R, MODE, V, 4>(a, variant, j, boff, stride, acc, g); j += 4; }
+  for (; j + 4 <= n; j += 4) fold_batch<R, MODE, V, 4>(a, variant, j, boff, stride, acc, g);
   if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, variant, j, boff, stride, acc, g); j += 2; }
   if (j < n) fold_batch<R, MODE, V, 1>(a, variant, j, boff, stride, acc, g);
 #pragma unroll

@@ -46,9 +46,13 @@ def _element_unit(dtype: str, unit_bytes: int) -> int:
 
 def allreduce(inputs: list[np.ndarray], nnodes: int, algo: str, nchannels: int,
               chunk_bytes: int, dtype: str, op: str, unit_bytes: int = UNIT_BYTES,
-              stats: dict | None = None) -> list[np.ndarray]:
+              stats: dict | None = None, pattern: str = "tree", intra=None) -> list[np.ndarray]:
     """All-reduce ``inputs`` (one array per rank); returns one array per rank.
 
+    ``pattern`` and ``intra`` (per-channel rank orders) are passed to
+    :func:`oracle.topology.build_topology`.  The ring of channel c visits the
+    ranks in ``intra[c]`` order: ring position p is rank ``intra[c][p]``, and
+    the ring steps of ``oracle.ring`` run over positions.
     ``stats``, if given, receives ``sent_elems`` (per-rank elements sent).
     """
     n, count = _check_inputs(inputs, dtype)
@@ -66,16 +70,19 @@ def allreduce(inputs: list[np.ndarray], nnodes: int, algo: str, nchannels: int,
     def cp(a):
         return np.array(a, copy=True)
 
+    topo = topology.build_topology(n, nnodes, nchannels, pattern, intra)
     if algo == "ring":
-        for grid_offset, ch_count in partition.channel_ranges(count, unit, nchannels):
+        for c, (grid_offset, ch_count) in enumerate(partition.channel_ranges(count, unit, nchannels)):
+            order = topo.channels[c].order
             for blocks in partition.ring_loops(grid_offset, ch_count, n, chunk_count, unit):
-                bufs = [[inputs[r][o:o + ln].copy() for (o, ln) in blocks] for r in range(n)]
-                ring.ring_allreduce_blocks(bufs, comb, cp, sent=sent, size=len)
-                for r in range(n):
-                    for (o, ln), blk in zip(blocks, bufs[r]):
-                        outputs[r][o:o + ln] = blk
+                bufs = [[inputs[order[p]][o:o + ln].copy() for (o, ln) in blocks] for p in range(n)]
+                pos_sent = [0] * n
+                ring.ring_allreduce_blocks(bufs, comb, cp, sent=pos_sent, size=len)
+                for p in range(n):
+                    sent[order[p]] += pos_sent[p]
+                    for (o, ln), blk in zip(blocks, bufs[p]):
+                        outputs[order[p]][o:o + ln] = blk
     elif algo == "tree":
-        topo = topology.build_topology(n, nnodes, nchannels)
         for c, (grid_offset, ch_count) in enumerate(partition.channel_ranges(count, unit, nchannels)):
             ch = topo.channels[c]
             for o, ln in partition.tree_chunks(grid_offset, ch_count, chunk_count):
@@ -92,7 +99,7 @@ def allreduce(inputs: list[np.ndarray], nnodes: int, algo: str, nchannels: int,
 
 def allreduce_at(inputs: list[np.ndarray], index: np.ndarray, nnodes: int, algo: str,
                  nchannels: int, chunk_bytes: int, dtype: str, op: str,
-                 unit_bytes: int = UNIT_BYTES) -> np.ndarray:
+                 unit_bytes: int = UNIT_BYTES, pattern: str = "tree", intra=None) -> np.ndarray:
     """The all-reduce result at element positions ``index`` only.
 
     Each position is placed in its channel and loop/chunk by the same
@@ -118,7 +125,7 @@ def allreduce_at(inputs: list[np.ndarray], index: np.ndarray, nnodes: int, algo:
         return np.array(a, copy=True)
 
     ranges = partition.channel_ranges(count, unit, nchannels)
-    topo = topology.build_topology(n, nnodes, nchannels) if algo == "tree" else None
+    topo = topology.build_topology(n, nnodes, nchannels, pattern, intra)
     for c, (grid_offset, ch_count) in enumerate(ranges):
         in_ch = (index >= grid_offset) & (index < grid_offset + ch_count)
         if not in_ch.any():
@@ -128,7 +135,8 @@ def allreduce_at(inputs: list[np.ndarray], index: np.ndarray, nnodes: int, algo:
                 sel = [np.nonzero((index >= o) & (index < o + ln))[0] for (o, ln) in blocks]
                 if not any(s.size for s in sel):
                     continue
-                bufs = [[inputs[r][index[s]] for s in sel] for r in range(n)]
+                order = topo.channels[c].order
+                bufs = [[inputs[order[p]][index[s]] for s in sel] for p in range(n)]
                 ring.ring_allreduce_blocks(bufs, comb, cp)
                 for s, blk in zip(sel, bufs[0]):
                     out[s] = blk

@@ -19,11 +19,28 @@ Sources (page title, then section):
     symmetry, one root, N-1 edges, no cycle, every rank reaches the root).
   - "直接执行源码中的 DTree": the probe table of roots and depths.
 
+* "NCCL 专家课程 13", section "节点内先形成链" (the preset code): per channel
+  the chain follows that channel's intra-node order, and the head pattern
+  picks which chain positions carry the node-level edges: the parent edge
+  always leaves from position 0; the child edges arrive at position 0 for the
+  plain tree pattern, at position 1 for the split pattern, and at position 1
+  (child0) and 0 (child1) for the balanced pattern.
+* "NCCL代码分析", section "Tree搜索": the three intra-node tree
+  patterns (tree, split tree, balanced tree).
+* Section "节点间连接" (connectTrees): a node's parent head links up to the
+  parent node's child0 head or child1 head, as the node's child type says; a
+  node's child0 (child1) head takes the parent head of its child0 (child1)
+  node as a child.
+
 Readings where the pages are silent (each listed in the design doc):
 
-* The intra-node order is the identity (local i = rank node*L + i) for every
-  channel; the head pattern is the plain tree pattern, so the parent head and
-  both child heads are local index 0.
+* The intra-node order of every channel is given by the caller (the pages
+  obtain it from a hardware graph search); by default it is the identity
+  (local i = rank node*L + i).  The ring of a channel runs through node 0's
+  order, then node 1's, and so on (the ring joins the nodes' channels end to
+  end).
+* The split and balanced patterns name chain position 1, so they need at
+  least two ranks per node.
 * Attaching a parent writes ``up``; attaching a child writes the first empty
   ``down`` slot, children taken in the order child0 then child1; a full record
   is an error.
@@ -33,7 +50,8 @@ Readings where the pages are silent (each listed in the design doc):
 
 Pins (tests/test_oracle_topology.py): the probe table, the 4-node drawings,
 the chain roles, the structural assertions for every shape up to 64 ranks and
-the depth formula values that the pages work out.
+the depth formula values that the pages work out, the per-channel chains of
+the pages' 4-GPU table, and hand-worked records of the three patterns.
 """
 
 from __future__ import annotations
@@ -121,6 +139,7 @@ class ChannelTree:
     down: list[list[int]]
     tree_index: int            # 0 or 1: which node-level tree this channel uses
     depth: int                 # the pages' approximation, metadata only
+    order: list[int] = field(default_factory=list)   # ring / chain order of the ranks
 
     @property
     def root(self) -> int:
@@ -150,6 +169,7 @@ class Topology:
     nnodes: int
     nchannels: int
     channels: list[ChannelTree] = field(default_factory=list)
+    pattern: str = "tree"
 
     @property
     def local_ranks(self) -> int:
@@ -172,40 +192,85 @@ def _attach_down(down: list[list[int]], r: int, child: int) -> None:
     raise TopologyError(f"rank {r} has no free child slot for {child}")
 
 
-def build_topology(nranks: int, nnodes: int, nchannels: int) -> Topology:
+PATTERNS = ("tree", "split", "balanced")
+
+
+def head_positions(pattern: str) -> tuple[int, int, int]:
+    """Chain positions of the (parent, child0, child1) heads of a node
+    (section "节点内先形成链")."""
+    if pattern == "tree":
+        return 0, 0, 0
+    if pattern == "split":
+        return 0, 1, 1
+    if pattern == "balanced":
+        return 0, 1, 0
+    raise ValueError(f"unknown pattern {pattern!r}")
+
+
+def _check_intra(intra, nranks: int, nnodes: int, nchannels: int) -> list[list[int]]:
+    L = nranks // nnodes
+    if intra is None:
+        return [list(range(nranks)) for _ in range(nchannels)]
+    intra = [list(map(int, row)) for row in intra]
+    if len(intra) != nchannels:
+        raise ValueError("need one intra-node order per channel")
+    for row in intra:
+        if len(row) != nranks:
+            raise ValueError("an intra-node order lists every rank once")
+        for m in range(nnodes):
+            if sorted(row[m * L:(m + 1) * L]) != list(range(m * L, (m + 1) * L)):
+                raise ValueError(f"order of node {m} is not a permutation of its ranks")
+    return intra
+
+
+def build_topology(nranks: int, nnodes: int, nchannels: int, pattern: str = "tree",
+                   intra=None) -> Topology:
     """Per-channel tree records for N ranks on M nodes (L = N/M per node).
 
-    Ranks are node-major: rank = node*L + local.  Inside each node the ranks
-    form a chain in identity order (section "节点内先形成链").  The head of
-    every node is local index 0; the node-level parent and children of the
-    channel's tree are attached to it, parent first, then child0, then child1,
-    each child taking the first empty slot (section "节点间连接").
+    Ranks are node-major: rank = node*L + local.  ``intra[c]`` lists, node
+    after node, the ranks of each node in channel c's chain order (default:
+    identity).  Inside each node the ranks form a chain in that order: parent
+    = previous, first child = next (section "节点内先形成链").  The node-level
+    edges of the channel's tree then go to the heads that ``pattern`` names:
+    each node's parent head links up to the parent node's child0 or child1
+    head (by the node's child type); each node's child0 and child1 heads take
+    the parent heads of the child0 and child1 nodes as children, child0 first,
+    each in the first empty slot (section "节点间连接").
     """
     if nranks < 1 or nnodes < 1 or nranks % nnodes != 0:
         raise ValueError("need nranks >= 1, nnodes >= 1 and nnodes dividing nranks")
     if nchannels < 1:
         raise ValueError("need at least one channel")
     L = nranks // nnodes
+    pos_parent, pos_child0, pos_child1 = head_positions(pattern)
+    if max(pos_parent, pos_child0, pos_child1) >= L:
+        raise ValueError(f"pattern {pattern!r} needs at least two ranks per node")
+    orders = _check_intra(intra, nranks, nnodes, nchannels)
     depth = L - 1 + log2i(nnodes)
     node_trees = [dtree(nnodes, m) for m in range(nnodes)]
     n_first = (nchannels + 1) // 2
-    topo = Topology(nranks, nnodes, nchannels)
+    topo = Topology(nranks, nnodes, nchannels, pattern=pattern)
     for c in range(nchannels):
         t = 0 if c < n_first else 1
+        order = orders[c]
         up = [-1] * nranks
         down = [[-1, -1, -1] for _ in range(nranks)]
-        for node in range(nnodes):
-            for i in range(L):
-                r = node * L + i
-                up[r] = r - 1 if i > 0 else -1
-                down[r][0] = r + 1 if i < L - 1 else -1
-        for node in range(nnodes):
-            head = node * L
-            parent, child0, child1, _ = node_trees[node][t]
-            _attach_up(up, head, -1 if parent == -1 else parent * L)
-            _attach_down(down, head, -1 if child0 == -1 else child0 * L)
-            _attach_down(down, head, -1 if child1 == -1 else child1 * L)
-        topo.channels.append(ChannelTree(up, down, t, depth))
+        chain = [order[m * L:(m + 1) * L] for m in range(nnodes)]
+        for m in range(nnodes):
+            for i, r in enumerate(chain[m]):
+                up[r] = chain[m][i - 1] if i > 0 else -1
+                down[r][0] = chain[m][i + 1] if i < L - 1 else -1
+        parent_head = [chain[m][pos_parent] for m in range(nnodes)]
+        child_head = [(chain[m][pos_child0], chain[m][pos_child1]) for m in range(nnodes)]
+        for m in range(nnodes):
+            parent, child0, child1, ctype = node_trees[m][t]
+            if parent != -1:
+                _attach_up(up, parent_head[m], child_head[parent][ctype])
+            if child0 != -1:
+                _attach_down(down, child_head[m][0], parent_head[child0])
+            if child1 != -1:
+                _attach_down(down, child_head[m][1], parent_head[child1])
+        topo.channels.append(ChannelTree(up, down, t, depth, order=list(order)))
     return topo
 
 

@@ -1,6 +1,7 @@
 """Pins of the oracle ring and tree simulators (CPU only)."""
 
 import numpy as np
+import pytest
 
 from oracle import allreduce as A
 from oracle import ring as R
@@ -81,6 +82,47 @@ def test_chain_fold_order_pin():
     out = A.allreduce(inputs, 1, "tree", 1, 512 * 1024, "f32", "sum")
     for o in out:
         assert o.tolist() == pin["expect"]
+
+
+def test_permuted_ring_fold_order_pin():
+    pin = _order_pin("RING3P")
+    order = [int(x) for x in pin["order"]]
+    inputs = [np.full(12, v, dtype=np.float32) for v in pin["inputs"]]
+    out = A.allreduce(inputs, 1, "ring", 1, 512 * 1024, "f32", "sum", intra=[order])
+    for o in out:
+        assert o.tolist() == pin["expect"]
+    # the sampled form agrees
+    at = A.allreduce_at(inputs, np.arange(12), 1, "ring", 1, 512 * 1024, "f32", "sum", intra=[order])
+    assert at.tolist() == pin["expect"]
+
+
+def test_permuted_chain_fold_order_pin():
+    pin = _order_pin("CHAIN4P")
+    order = [int(x) for x in pin["order"]]
+    inputs = [np.full(4, v, dtype=np.float32) for v in pin["inputs"]]
+    out = A.allreduce(inputs, 1, "tree", 1, 512 * 1024, "f32", "sum", intra=[order])
+    for o in out:
+        assert o.tolist() == pin["expect"]
+
+
+@pytest.mark.parametrize("pattern", ["tree", "split", "balanced"])
+def test_head_pattern_fold_order_pin(pattern):
+    pin = _order_pin("HEADS4")
+    inputs = [np.full(4, v, dtype=np.float32) for v in pin["inputs"]]
+    out = A.allreduce(inputs, 2, "tree", 1, 512 * 1024, "f32", "sum", pattern=pattern)
+    for o in out:
+        assert o.tolist() == pin["expect_" + pattern]
+    at = A.allreduce_at(inputs, np.arange(4), 2, "tree", 1, 512 * 1024, "f32", "sum", pattern=pattern)
+    assert at.tolist() == pin["expect_" + pattern]
+
+
+def test_ring_order_sends_per_rank():
+    # A permuted ring moves the same volume: every rank sends 2(N-1) blocks.
+    n, count = 4, 64
+    inputs = [np.zeros(count, dtype=np.int32) for _ in range(n)]
+    stats = {}
+    A.allreduce(inputs, 1, "ring", 1, 16 * 1024, "i32", "sum", stats=stats, intra=[[2, 0, 3, 1]])
+    assert stats["sent_elems"] == [2 * (n - 1) * count // n] * n
 
 
 def test_tree_symbolic_every_shape_reaches_everyone():

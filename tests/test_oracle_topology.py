@@ -185,3 +185,143 @@ def test_step_counts_figure():
         n, ring_steps, tree_steps = (int(x) for x in line.split())
         assert 2 * (n - 1) == ring_steps
         assert 2 * T.node_tree_depth(n, 0) == tree_steps
+
+
+# ---------------------------------------------------------------------------
+# Per-channel chain orders and head patterns.
+
+def _chain_walk(ch):
+    """Root-to-leaf walk along first children (a chain has one path)."""
+    out, x = [], ch.root
+    while x != -1:
+        out.append(x)
+        kids = ch.children(x)
+        x = kids[0] if kids else -1
+    return out
+
+
+def test_v100_channel_chains_table():
+    # "NCCL 专家课程 13", section "从 GRAPH 日志复原 active tree": 12 channels per
+    # world size, each a chain in its own order; 108 records in all.
+    rows = [ln.split() for ln in golden_lines("v100_channel_chains.txt") if ln.startswith("CHAINS")]
+    records = int(next(ln.split()[1] for ln in golden_lines("v100_channel_chains.txt")
+                       if ln.startswith("RECORDS")))
+    total = 0
+    for n in (2, 3, 4):
+        intra = [None] * 12
+        want = {}
+        for _, world, chans, order, depth, fan in rows:
+            if int(world) != n:
+                continue
+            order = [int(x) for x in order.split("-")]
+            for c in map(int, chans.split(",")):
+                intra[c] = order
+                want[c] = (order, int(depth), int(fan))
+        assert all(o is not None for o in intra), n
+        topo = T.build_topology(n, 1, 12, intra=intra)
+        for c, ch in enumerate(topo.channels):
+            T.check_tree(ch)
+            order, depth, fan = want[c]
+            assert ch.root == order[0]
+            assert _chain_walk(ch) == order
+            assert ch.true_depth() == depth
+            assert max(len(ch.children(r)) for r in range(n)) == fan
+            total += n
+        distinct = {tuple(_chain_walk(ch)) for ch in topo.channels}
+        assert len(distinct) == {2: 2, 3: 2, 4: 3}[n]
+    assert total == records
+
+
+def test_head_patterns_hand_worked_3x2():
+    intra = [1, 0, 2, 3, 5, 4]
+    got = {}
+    for pattern in T.PATTERNS:
+        topo = T.build_topology(6, 3, 2, pattern, [intra, intra])
+        assert [ch.tree_index for ch in topo.channels] == [0, 1]
+        for ch in topo.channels:
+            T.check_tree(ch)
+            got[(pattern, ch.tree_index)] = (ch.up, ch.down)
+    seen = 0
+    for line in golden_lines("head_patterns_3x2.txt"):
+        left, right = line.split("|")
+        pattern, tree, _, *ups = left.split()
+        downs = [[int(v) for v in d.split(",")] for d in right.split()[1:]]
+        assert got[(pattern, int(tree))] == ([int(u) for u in ups], downs), (pattern, tree)
+        seen += 1
+    assert seen == 6
+
+
+def _random_orders(rng, n, m, nch):
+    L = n // m
+    out = []
+    for _ in range(nch):
+        row = []
+        for node in range(m):
+            row += [int(x) for x in rng.permutation(range(node * L, (node + 1) * L))]
+        out.append(row)
+    return out
+
+
+@pytest.mark.parametrize("pattern", ["tree", "split", "balanced"])
+@pytest.mark.parametrize("n,m", [(4, 2), (6, 3), (8, 2), (8, 4), (12, 4), (16, 2), (16, 8), (24, 3),
+                                 (32, 4), (30, 5), (64, 8), (64, 32), (18, 9), (10, 5), (14, 7)])
+def test_pattern_invariants_random_orders(pattern, n, m):
+    # Contracting every node to one vertex gives the node-level tree of the
+    # channel; inside a node the edges are the chain in the channel's order;
+    # the edge to the parent node leaves from chain position 0 and lands on
+    # the parent node's child0 or child1 head.
+    import numpy as np
+    rng = np.random.default_rng(n * 1000 + m)
+    L = n // m
+    pos_p, pos_c0, pos_c1 = T.head_positions(pattern)
+    nch = 4
+    intra = _random_orders(rng, n, m, nch)
+    topo = T.build_topology(n, m, nch, pattern, intra)
+    for c, ch in enumerate(topo.channels):
+        T.check_tree(ch)
+        assert ch.order == intra[c]
+        chains = [intra[c][k * L:(k + 1) * L] for k in range(m)]
+        pos = {r: (k, chains[k].index(r)) for k in range(m) for r in chains[k]}
+        for r in range(n):
+            k, i = pos[r]
+            u = ch.up[r]
+            node_parent = T.dtree(m, k)[ch.tree_index][0]
+            if i > 0:
+                assert u == chains[k][i - 1]
+            elif node_parent == -1:
+                assert u == -1
+            else:
+                ctype = T.dtree(m, k)[ch.tree_index][3]
+                kp, ip = pos[u]
+                assert kp == node_parent
+                assert ip == (pos_c0 if ctype == 0 else pos_c1)
+            # children: the chain successor first, then the child nodes' heads
+            kids = ch.children(r)
+            want = [chains[k][i + 1]] if i < L - 1 else []
+            _, c0, c1, _ = T.dtree(m, k)[ch.tree_index]
+            if c0 != -1 and i == pos_c0:
+                want.append(chains[c0][pos_p])
+            if c1 != -1 and i == pos_c1:
+                want.append(chains[c1][pos_p])
+            assert kids == want, (c, r)
+
+
+def test_pattern_needs_two_ranks_per_node_and_valid_orders():
+    with pytest.raises(ValueError):
+        T.build_topology(4, 4, 2, "split")
+    with pytest.raises(ValueError):
+        T.build_topology(4, 4, 2, "balanced")
+    T.build_topology(4, 4, 2, "tree")
+    with pytest.raises(ValueError):
+        T.build_topology(4, 2, 1, "tree", [[0, 2, 1, 3]])   # rank 2 is not on node 0
+    with pytest.raises(ValueError):
+        T.build_topology(4, 1, 2, "tree", [[0, 1, 2, 3]])   # one order per channel
+    with pytest.raises(ValueError):
+        T.build_topology(4, 1, 1, "ring", None)
+
+
+def test_identity_orders_match_the_default():
+    for n, m in ((8, 1), (16, 16), (32, 4), (6, 3)):
+        a = T.build_topology(n, m, 4)
+        b = T.build_topology(n, m, 4, "tree", [list(range(n))] * 4)
+        assert [(c.up, c.down) for c in a.channels] == [(c.up, c.down) for c in b.channels]

@@ -18,7 +18,8 @@
 namespace emu {
 
 // Defined in fused.hip / stepwise.hip.
-hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, int grid, hipStream_t stream);
+hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows,
+                        int grid, hipStream_t stream);
 int fused_tile_vectors();
 hipError_t launch_stepwise(bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
                            size_t lds, hipStream_t s);
@@ -26,8 +27,6 @@ int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds);
 int stepwise_vectors_per_lane(bool ring);
 
 namespace {
-
-constexpr int kFusedRingFold = 0, kFusedTreeFold = 1, kFusedTreeProgram = 2;
 
 long env_long(const char* name, long fallback) {
   const char* v = std::getenv(name);
@@ -50,11 +49,11 @@ struct DeviceBuffer {
 
 struct Plan {
   // fused
-  DeviceBuffer tiles;
+  DeviceBuffer tiles, rows;
   uint32_t ntiles = 0;
   int fused_grid = 0;
   // stepwise
-  DeviceBuffer tasks, table;
+  DeviceBuffer tasks, table, orders;
   uint32_t ntasks = 0;
   int group = 0, block = 0, grid = 0;
   size_t lds = 0;
@@ -67,13 +66,12 @@ struct Comm {
   bool fused = false;
   size_t chunk_bytes = 0;
   Topology topo;
-  TreeProgram prog{};
-  int tree_mode = kFusedTreeProgram;
+  FusedOrders orders;   // fused mode: how each tile names its order
   // (device, count, dtype, op) -> plan
   std::map<std::tuple<int, uint64_t, int, int>, std::unique_ptr<Plan>> plans;
 };
 
-using CommKey = std::tuple<int, int, int, int, size_t>;
+using CommKey = std::tuple<int, int, int, int, size_t, int, std::vector<int>>;
 std::map<CommKey, std::unique_ptr<Comm>> g_comms;   // built communicators, reused on re-init
 Comm* g_active = nullptr;
 constexpr size_t kMaxCachedComms = 16;
@@ -109,9 +107,10 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   if (c.fused) {
     std::vector<Tile> tiles;
     const uint64_t tile_elems = (uint64_t)fused_tile_vectors() * unit;
-    build_fused_tiles(c.topo, c.algo, count, unit, chunk_count, tile_elems, &tiles);
+    build_fused_tiles(c.topo, c.algo, c.orders, count, unit, chunk_count, tile_elems, &tiles);
     p->ntiles = (uint32_t)tiles.size();
     if (int e = p->tiles.upload(tiles.data(), tiles.size() * sizeof(Tile))) return e;
+    if (int e = p->rows.upload(c.orders.rows.data(), c.orders.rows.size() * sizeof(uint32_t))) return e;
     const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 64);
     p->fused_grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntiles, (uint64_t)cus * per_cu));
     return EMU_SUCCESS;
@@ -124,10 +123,11 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   const size_t lds_limit = lds_per_block(dev);
   p->group = (int)env_long("EMU_STEP_GROUP", 64);   // tuning override; must be a power of two
   if (p->group > 64 || (p->group & (p->group - 1))) p->group = 64;
-  // LDS: ring 2 parities of slots plus 2 x N staged block descriptors, tree
-  // 2 parities x (up, down) slots.
+  // LDS: ring 2 parities of slots plus 2 x N staged block descriptors and
+  // 2 staged ring orders, tree 2 parities x (up, down) slots.
   auto lds_of = [&](int g) {
-    return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes + (ring ? 2u * n * sizeof(RingLoopBlock) : 0u);
+    return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes +
+           (ring ? 2u * n * sizeof(RingLoopBlock) + 2u * kMaxRanks : 0u);
   };
   while (p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
   if (n * p->group > 1024 || lds_of(p->group) > lds_limit) return EMU_ERR_INTERNAL;
@@ -137,11 +137,13 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   if (ring) {
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
+    std::vector<uint8_t> orders;
     if (count / slice_elems >= ((uint64_t)1 << 32)) return EMU_ERR_INVALID_ARGUMENT;   // cell index is 32-bit
-    build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks);
+    build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks, &orders);
     p->ntasks = (uint32_t)tasks.size();
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
     if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
+    if (int e = p->orders.upload(orders.data(), orders.size())) return e;
   } else {
     // One pipeline per resident workgroup (tasks per CU = occupancy, or the
     // tuning override EMU_TREE_TASKS_PER_CU).
@@ -172,7 +174,8 @@ using namespace emu;
 
 extern "C" {
 
-int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes) {
+int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes, int pattern,
+                        const int* intra) {
   const int base = algo & 0xFF;
   const int mode = algo & ~0xFF;
   if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE) return EMU_ERR_INVALID_ARGUMENT;
@@ -182,7 +185,11 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
   if (nranks < 1 || nranks > kMaxRanks || nnodes < 1 || nranks % nnodes != 0 || nchannels < 1 ||
       nchannels > kMaxChannels)
     return EMU_ERR_INVALID_ARGUMENT;
-  const CommKey key{nranks, nnodes, algo, nchannels, chunk_bytes};
+  // The key holds the orders as given (identity when intra is NULL), so
+  // equal graphs share one cached communicator.
+  std::vector<int> order((size_t)nchannels * nranks);
+  for (size_t i = 0; i < order.size(); ++i) order[i] = intra ? intra[i] : (int)(i % nranks);
+  const CommKey key{nranks, nnodes, algo, nchannels, chunk_bytes, pattern, order};
   auto it = g_comms.find(key);
   if (it != g_comms.end()) {
     g_active = it->second.get();
@@ -195,24 +202,8 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
   c->algo = base == EMU_ALGO_RING ? Algo::Ring : Algo::Tree;
   c->fused = mode == EMU_MODE_FUSED;
   c->chunk_bytes = chunk_bytes;
-  if (int e = build_topology(nranks, nnodes, nchannels, &c->topo)) return e;
-  if (c->algo == Algo::Tree) {
-    // Tree 0 and tree 1 programs from the first channel of each kind.
-    bool all_pure = true;
-    for (int t = 0; t < 2; ++t) {
-      const ChannelTopology* ch = nullptr;
-      for (const auto& cc : c->topo.channels)
-        if (cc.tree_index == t) { ch = &cc; break; }
-      if (!ch) ch = &c->topo.channels[0];
-      int nregs = 0;
-      bool pure = false;
-      if (int e = compile_tree_program(*ch, c->prog.perm[t], c->prog.instr[t], &nregs, &pure)) return e;
-      c->prog.pure_fold[t] = pure ? 1 : 0;
-      c->prog.nregs[t] = (uint8_t)nregs;
-      all_pure = all_pure && pure;
-    }
-    c->tree_mode = all_pure ? kFusedTreeFold : kFusedTreeProgram;
-  }
+  if (int e = build_topology(nranks, nnodes, nchannels, pattern, order.data(), &c->topo)) return e;
+  if (int e = build_fused_orders(c->topo, c->algo, &c->orders)) return e;
   if (g_comms.size() >= kMaxCachedComms) {
     // Drop every cached communicator except the active one.  Their device
     // tables may still be read by enqueued kernels: wait for the device first.
@@ -227,6 +218,10 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
   g_active = c.get();
   g_comms[key] = std::move(c);
   return EMU_SUCCESS;
+}
+
+int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes) {
+  return emu_comm_init_graph(nranks, nnodes, algo, nchannels, chunk_bytes, EMU_PATTERN_TREE, nullptr);
 }
 
 int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype, int op,
@@ -270,18 +265,22 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
   hipError_t err;
   if (c->fused) {
     FusedArgs a{};
-    for (int r = 0; r < n; ++r) { a.send[r] = sendbufs[r]; a.recv[r] = recvbufs[r]; }
-    a.tiles = static_cast<const Tile*>(p.tiles.ptr);
+    const FusedOrders& ord = c->orders;
+    for (int r = 0; r < n; ++r) {
+      // kRotate folds pointer j as the j-th rank of the shared order
+      a.send[r] = sendbufs[ord.mode == kRotate ? ord.rotate_perm[r] : r];
+      a.recv[r] = recvbufs[r];
+    }
     a.ntiles = p.ntiles;
     a.nranks = (uint32_t)n;
-    a.prog = c->prog;
-    const int mode = c->algo == Algo::Ring ? kFusedRingFold : c->tree_mode;
-    err = launch_fused(t, o, mode, a, p.fused_grid, s);
+    err = launch_fused(t, o, ord.mode, a, static_cast<const Tile*>(p.tiles.ptr),
+                       static_cast<const uint32_t*>(p.rows.ptr), p.fused_grid, s);
   } else {
     StepArgs a{};
     for (int r = 0; r < n; ++r) { a.send[r] = sendbufs[r]; a.recv[r] = recvbufs[r]; }
     a.tasks = p.tasks.ptr;
     a.table = p.table.ptr;
+    a.orders = static_cast<const uint8_t*>(p.orders.ptr);
     a.count = count;
     a.ntasks = p.ntasks;
     a.nranks = (uint32_t)n;

@@ -27,10 +27,10 @@ inline int elem_size(DType t) {
   return 0;
 }
 
-// A contiguous element range evaluated with one order program ("variant"):
-// for the ring, the rank whose block it is (the fold starts there); for the
-// tree, the index of the node-level tree (0 or 1) of its channel.  A tile
-// never straddles two variants.
+// A contiguous element range evaluated with one order ("variant"), whose
+// meaning depends on the fused mode (FusedMode): the rank-chunk index k for
+// a rotated fold, or (row << 8) | k for the order rows.  A tile never
+// straddles two variants.
 struct Tile {
   uint64_t start;     // first element
   uint32_t nelem;     // elements in the tile
@@ -38,25 +38,25 @@ struct Tile {
 };
 static_assert(sizeof(Tile) == 16, "tile layout");
 
-// Fused tree program.  Inputs are consumed in the order perm[0..N); input j
-// goes to register d = (instr >> 1) & 7: loaded if bit 0 is clear, folded
-// in (R[d] = R[d] op x) if set; then (instr >> 4) cascaded register folds
-// R[d-1] = R[d-1] op R[d], R[d-2] = R[d-2] op R[d-1], ...  The result ends
-// in R[0].
-struct TreeProgram {
-  uint8_t perm[2][kMaxRanks];
-  uint8_t instr[2][kMaxRanks];
-  uint8_t pure_fold[2];       // 1: plain left fold (all inputs folded into R[0])
-  uint8_t nregs[2];
-};
+// Fused modes.
+//  kRotate:  input j of variant k is rank (k + j) mod N of the pointer
+//            arrays, which the host passes already permuted into the one
+//            order every channel shares; a plain left fold.
+//  kFold:    input j is rank rows[row][k + j] & 0xFF; a plain left fold.
+//  kProgram: input j is rank rows[row][j] & 0xFF, consumed by the register
+//            program in bits 8..15 of the entry: it goes to register
+//            d = (w >> 1) & 7, loaded if bit 0 of w is clear, folded in
+//            (R[d] = R[d] op x) if set; then (w >> 4) cascaded register
+//            folds R[d-1] = R[d-1] op R[d], R[d-2] = R[d-2] op R[d-1], ...
+//            The result ends in R[0].
+enum FusedMode : int { kRotate = 0, kFold = 1, kProgram = 2 };
+constexpr int kRowLen = 2 * kMaxRanks;   // a ring row holds its order twice: k + j needs no wrap
 
 struct FusedArgs {
   const void* send[kMaxRanks];
   void* recv[kMaxRanks];
-  const Tile* tiles;
   uint32_t ntiles;
   uint32_t nranks;
-  TreeProgram prog;
 };
 
 // Stepwise ring: one task = slice q of every rank-chunk of one ring loop.
@@ -68,14 +68,16 @@ struct RingLoopBlock {
 struct RingTask {
   uint32_t loop;      // index into the loop table (nranks blocks per loop)
   uint32_t slice;     // slice index inside each block
+  uint32_t ring;      // the loop's ring order: row of the order table
+  uint32_t pad;
 };
 
 // Stepwise tree: one task = a run of consecutive slices of the message that
-// all use one node-level tree.
+// all use one tree (channels with identical records).
 struct TreeTask {
   uint64_t start;     // first element
   uint32_t nelem;     // elements covered
-  uint32_t channel;   // a channel of the task's node-level tree
+  uint32_t channel;   // a channel of the task's tree
 };
 // Tree record of one rank in one channel, plus its distance from the root.
 struct TreeNode {
@@ -91,6 +93,7 @@ struct StepArgs {
   void* recv[kMaxRanks];
   const void* tasks;          // RingTask* or TreeTask*
   const void* table;          // RingLoopBlock* (ring) or TreeNode* (tree, [nch][nranks])
+  const uint8_t* orders;      // ring: [rings][kMaxRanks], position p -> rank
   uint64_t count;             // elements per rank
   uint32_t ntasks;
   uint32_t nranks;

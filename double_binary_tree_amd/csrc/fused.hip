@@ -4,19 +4,20 @@
 // the result to every rank's receive buffer.  2*N*S bytes in total, no LDS.
 //
 // Orders (see the oracle and the pages):
-//  * ring: a rank-chunk k is folded x_k, x_{k+1}, ..., x_{k-1} (the block's
-//    journey through the reduce-scatter steps of page "all-reduce 每张卡要发
-//    多少数据? ring 和 tree 有什么区别?", Figure 1);
+//  * ring: rank-chunk k of a channel whose ring visits ranks o_0, o_1, ...
+//    is folded x_{o_k}, x_{o_{k+1}}, ..., x_{o_{k-1}} (the block's journey
+//    through the reduce-scatter steps of page "all-reduce 每张卡要发多少数据?
+//    ring 和 tree 有什么区别?", Figure 1);
 //  * tree: the expression of the channel's tree (reduce-up of page "NCCL
 //    专家课程 13", section "runTreeSplit 如何流水"), compiled on the host into
 //    a register program; a chain is a plain fold from the leaf up.
-// Tiles never straddle two orders, so all control flow below is uniform
-// (scalar) and only the element positions are per lane.
+// The three ways to name the order are the FusedMode values: a rotation of
+// host-permuted pointers when every channel shares one order, else rows of
+// a small order table.  Tiles never straddle two orders, so all control
+// flow below is uniform (scalar) and only the element positions are per lane.
 #include "device_ops.h"
 
 namespace emu {
-
-enum FusedMode : int { kRingFold = 0, kTreeFold = 1, kTreeProgram = 2 };
 
 #ifndef EMU_FUSED_THREADS
 #define EMU_FUSED_THREADS 256
@@ -44,30 +45,32 @@ __device__ __forceinline__ void reg_fold_down(u32x4 (&g)[kMaxRegs], int d) {
   g[d] = R::op(g[d], g[d + 1]);
 }
 
-// Input j of the order program: the rank whose buffer it comes from.
+// Entry j of the order: the rank whose buffer input j comes from (bits
+// 0..7) and, for kProgram, its register instruction (bits 8..15).
 template <int MODE>
-__device__ __forceinline__ uint32_t input_rank(const FusedArgs& a, uint32_t variant, uint32_t j) {
-  if (MODE == kRingFold) {
+__device__ __forceinline__ uint32_t order_entry(const FusedArgs& a, const uint32_t* __restrict__ rows,
+                                                uint32_t variant, uint32_t j) {
+  if (MODE == kRotate) {
     const uint32_t r = variant + j;
     return r >= a.nranks ? r - a.nranks : r;
   }
-  return a.prog.perm[variant][j];
+  return rows[(variant >> 8) * kRowLen + (variant & 0xFF) + j];
 }
 
 // Register stack size: the program mode's stack; the fold modes need none.
 template <int MODE>
-constexpr int stack_regs() { return MODE == kTreeProgram ? kMaxRegs : 1; }
+constexpr int stack_regs() { return MODE == kProgram ? kMaxRegs : 1; }
 
 template <typename R, int MODE, int V>
-__device__ __forceinline__ void consume(const FusedArgs& a, uint32_t variant, uint32_t j, const u32x4 (&x)[V],
+__device__ __forceinline__ void consume(uint32_t entry, uint32_t j, const u32x4 (&x)[V],
                                         u32x4 (&acc)[V], u32x4 (&g)[stack_regs<MODE>()]) {
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const u32x4 val = R::pre(x[v]);
-    if constexpr (MODE == kTreeProgram) {
-      const uint32_t w = a.prog.instr[variant][j];
+    if constexpr (MODE == kProgram) {
+      const uint32_t w = entry >> 8;
       const int d = (w >> 1) & 7;
-      static_assert(MODE != kTreeProgram || V == 1, "program mode evaluates one position at a time");
+      static_assert(MODE != kProgram || V == 1, "program mode evaluates one position at a time");
       reg_fold_in<R>(g, d, (w & 1) != 0, val);
       const int pops = (int)(w >> 4);
       for (int p = 1; p <= pops; ++p) reg_fold_down<R>(g, d - p);
@@ -80,11 +83,15 @@ __device__ __forceinline__ void consume(const FusedArgs& a, uint32_t variant, ui
 // Fold inputs j .. j+B-1 at V whole-vector positions (byte offsets boff +
 // v*stride).  The B*V loads are unconditional and issued back to back.
 template <typename R, int MODE, int V, int B>
-__device__ __forceinline__ void fold_batch(const FusedArgs& a, uint32_t variant, uint32_t j, uint64_t boff,
-                                           uint32_t stride, u32x4 (&acc)[V], u32x4 (&g)[stack_regs<MODE>()]) {
+__device__ __forceinline__ void fold_batch(const FusedArgs& a, const uint32_t* __restrict__ rows, uint32_t variant,
+                                           uint32_t j, uint64_t boff, uint32_t stride, u32x4 (&acc)[V],
+                                           u32x4 (&g)[stack_regs<MODE>()]) {
+  uint32_t e[B];
   const void* src[B];
 #pragma unroll
-  for (int i = 0; i < B; ++i) src[i] = a.send[input_rank<MODE>(a, variant, j + i)];
+  for (int i = 0; i < B; ++i) e[i] = order_entry<MODE>(a, rows, variant, j + i);
+#pragma unroll
+  for (int i = 0; i < B; ++i) src[i] = a.send[e[i] & 0xFF];
   u32x4 x[B][V];
 #pragma unroll
   for (int i = 0; i < B; ++i)
@@ -98,40 +105,42 @@ __device__ __forceinline__ void fold_batch(const FusedArgs& a, uint32_t variant,
   __builtin_amdgcn_sched_barrier(0);
 #endif
 #pragma unroll
-  for (int i = 0; i < B; ++i) consume<R, MODE, V>(a, variant, j + i, x[i], acc, g);
+  for (int i = 0; i < B; ++i) consume<R, MODE, V>(e[i], j + i, x[i], acc, g);
 }
 
 // Evaluate V whole-vector positions.
 template <typename R, int MODE, int V>
-__device__ __forceinline__ void evaluate(const FusedArgs& a, uint32_t variant, uint64_t boff, uint32_t stride,
-                                         u32x4 (&out)[V]) {
+__device__ __forceinline__ void evaluate(const FusedArgs& a, const uint32_t* __restrict__ rows, uint32_t variant,
+                                         uint64_t boff, uint32_t stride, u32x4 (&out)[V]) {
   const uint32_t n = a.nranks;
   u32x4 acc[V];
   u32x4 g[stack_regs<MODE>()];
 #pragma unroll
   for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
   uint32_t j = 0;
-  for (; j + kBatch <= n; j += kBatch) fold_batch<R, MODE, V, kBatch>(a, variant, j, boff, stride, acc, g);
-  for (; j + 4 <= n; j += 4) fold_batch<R, MODE, V, 4>(a, variant, j, boff, stride, acc, g);
-  if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, variant, j, boff, stride, acc, g); j += 2; }
-  if (j < n) fold_batch<R, MODE, V, 1>(a, variant, j, boff, stride, acc, g);
+  for (; j + kBatch <= n; j += kBatch) fold_batch<R, MODE, V, kBatch>(a, rows, variant, j, boff, stride, acc, g);
+  for (; j + 4 <= n; j += 4) fold_batch<R, MODE, V, 4>(a, rows, variant, j, boff, stride, acc, g);
+  if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, rows, variant, j, boff, stride, acc, g); j += 2; }
+  if (j < n) fold_batch<R, MODE, V, 1>(a, rows, variant, j, boff, stride, acc, g);
 #pragma unroll
-  for (int v = 0; v < V; ++v) out[v] = R::post(MODE == kTreeProgram ? g[0] : acc[v]);
+  for (int v = 0; v < V; ++v) out[v] = R::post(MODE == kProgram ? g[0] : acc[v]);
 }
 
 // The one partial vector at the end of the message: `nbytes` valid bytes,
 // one rank at a time, 16-bit accesses.
 template <typename R, int MODE>
-__device__ __forceinline__ void partial_vector(const FusedArgs& a, uint32_t variant, uint64_t boff, int nbytes) {
+__device__ __forceinline__ void partial_vector(const FusedArgs& a, const uint32_t* __restrict__ rows,
+                                               uint32_t variant, uint64_t boff, int nbytes) {
   u32x4 acc[1];
   u32x4 g[stack_regs<MODE>()];
 #pragma unroll
   for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
   for (uint32_t j = 0; j < a.nranks; ++j) {
-    const u32x4 x[1] = {ld_part(a.send[input_rank<MODE>(a, variant, j)], boff, nbytes)};
-    consume<R, MODE, 1>(a, variant, j, x, acc, g);
+    const uint32_t e = order_entry<MODE>(a, rows, variant, j);
+    const u32x4 x[1] = {ld_part(a.send[e & 0xFF], boff, nbytes)};
+    consume<R, MODE, 1>(e, j, x, acc, g);
   }
-  const u32x4 res = R::post(MODE == kTreeProgram ? g[0] : acc[0]);
+  const u32x4 res = R::post(MODE == kProgram ? g[0] : acc[0]);
   for (uint32_t r = 0; r < a.nranks; ++r) st_part(a.recv[r], boff, nbytes, res);
 }
 
@@ -158,11 +167,11 @@ __device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, uin
 
 // A tile holds kFusedThreads * kVpt vectors; lane l owns vectors l, l + 256,
 // ... (each group of 64 lanes touches 1 KiB contiguous per rank).
-// The tile table comes as its own read-only argument so that the (uniform)
-// descriptor loads go through the scalar unit.
+// The tile table and the order rows come as their own read-only arguments
+// so that the (uniform) loads from them go through the scalar unit.
 template <typename R, int MODE, int ESZ>
-__global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs a,
-                                                                 const Tile* __restrict__ tiles) {
+__global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs a, const Tile* __restrict__ tiles,
+                                                                 const uint32_t* __restrict__ rows) {
   constexpr uint32_t unit = kVecBytes / ESZ;
   constexpr uint32_t stride = kFusedThreads * kVecBytes;   // bytes between a lane's vectors
   for (uint32_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
@@ -170,18 +179,18 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs
     const uint64_t base = tile.start * ESZ;
     const uint32_t lane_off = threadIdx.x * kVecBytes;
     if (tile.nelem == kFusedThreads * kVpt * unit) {
-      if (MODE == kTreeProgram) {
+      if (MODE == kProgram) {
         // The register stack is indexed dynamically; one position at a time
         // keeps it in VGPRs.
         for (int v = 0; v < kVpt; ++v) {
           u32x4 res[1];
-          evaluate<R, MODE, 1>(a, tile.variant, base + lane_off + (uint64_t)v * stride, 0, res);
+          evaluate<R, MODE, 1>(a, rows, tile.variant, base + lane_off + (uint64_t)v * stride, 0, res);
           store_all<1>(a, base + lane_off + (uint64_t)v * stride, 0, res);
         }
       } else {
-        constexpr int V = MODE == kTreeProgram ? 1 : kVpt;
+        constexpr int V = MODE == kProgram ? 1 : kVpt;
         u32x4 res[V];
-        evaluate<R, MODE, V>(a, tile.variant, base + lane_off, stride, res);
+        evaluate<R, MODE, V>(a, rows, tile.variant, base + lane_off, stride, res);
         store_all<V>(a, base + lane_off, stride, res);
       }
       continue;
@@ -197,44 +206,48 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs
       const uint64_t boff = pos * ESZ;
       if (end - pos >= unit) {
         u32x4 res[1];
-        evaluate<R, MODE, 1>(a, tile.variant, boff, 0, res);
+        evaluate<R, MODE, 1>(a, rows, tile.variant, boff, 0, res);
         store_all<1>(a, boff, 0, res);
       } else {
-        partial_vector<R, MODE>(a, tile.variant, boff, (int)((end - pos) * ESZ));
+        partial_vector<R, MODE>(a, rows, tile.variant, boff, (int)((end - pos) * ESZ));
       }
     }
   }
 }
 
 template <DType T, Op O, int MODE>
-static hipError_t launch_one(const FusedArgs& a, int grid, hipStream_t stream) {
+static hipError_t launch_one(const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
+                             hipStream_t stream) {
   hipLaunchKernelGGL((fused_allreduce<Red<T, O>, MODE, Unit<T>::esz>), dim3(grid), dim3(kFusedThreads),
-                     0, stream, a, a.tiles);
+                     0, stream, a, tiles, rows);
   return hipGetLastError();
 }
 
 template <DType T, Op O>
-static hipError_t launch_mode(int mode, const FusedArgs& a, int grid, hipStream_t stream) {
+static hipError_t launch_mode(int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
+                              hipStream_t stream) {
   switch (mode) {
-    case kRingFold: return launch_one<T, O, kRingFold>(a, grid, stream);
-    case kTreeFold: return launch_one<T, O, kTreeFold>(a, grid, stream);
-    default: return launch_one<T, O, kTreeProgram>(a, grid, stream);
+    case kRotate: return launch_one<T, O, kRotate>(a, tiles, rows, grid, stream);
+    case kFold: return launch_one<T, O, kFold>(a, tiles, rows, grid, stream);
+    default: return launch_one<T, O, kProgram>(a, tiles, rows, grid, stream);
   }
 }
 
 template <DType T>
-static hipError_t launch_op(Op op, int mode, const FusedArgs& a, int grid, hipStream_t stream) {
-  return op == Op::Sum ? launch_mode<T, Op::Sum>(mode, a, grid, stream)
-                       : launch_mode<T, Op::Max>(mode, a, grid, stream);
+static hipError_t launch_op(Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
+                            hipStream_t stream) {
+  return op == Op::Sum ? launch_mode<T, Op::Sum>(mode, a, tiles, rows, grid, stream)
+                       : launch_mode<T, Op::Max>(mode, a, tiles, rows, grid, stream);
 }
 
-hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, int grid, hipStream_t stream) {
+hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows,
+                        int grid, hipStream_t stream) {
   switch (t) {
-    case DType::I32: return launch_op<DType::I32>(op, mode, a, grid, stream);
-    case DType::I64: return launch_op<DType::I64>(op, mode, a, grid, stream);
-    case DType::F32: return launch_op<DType::F32>(op, mode, a, grid, stream);
-    case DType::F16: return launch_op<DType::F16>(op, mode, a, grid, stream);
-    case DType::BF16: return launch_op<DType::BF16>(op, mode, a, grid, stream);
+    case DType::I32: return launch_op<DType::I32>(op, mode, a, tiles, rows, grid, stream);
+    case DType::I64: return launch_op<DType::I64>(op, mode, a, tiles, rows, grid, stream);
+    case DType::F32: return launch_op<DType::F32>(op, mode, a, tiles, rows, grid, stream);
+    case DType::F16: return launch_op<DType::F16>(op, mode, a, tiles, rows, grid, stream);
+    case DType::BF16: return launch_op<DType::BF16>(op, mode, a, tiles, rows, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -58,8 +58,8 @@ std::vector<std::vector<Range>> ring_loops(const Range& ch, int nranks, uint64_t
   return loops;
 }
 
-void build_fused_tiles(const Topology& topo, Algo algo, uint64_t count, uint64_t unit,
-                       uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out) {
+void build_fused_tiles(const Topology& topo, Algo algo, const FusedOrders& orders, uint64_t count,
+                       uint64_t unit, uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out) {
   // Segments (start, length, variant) in element order, adjacent segments of
   // equal variant merged.
   struct Seg { uint64_t start, len; uint32_t variant; };
@@ -75,9 +75,9 @@ void build_fused_tiles(const Topology& topo, Algo algo, uint64_t count, uint64_t
   for (int c = 0; c < topo.nchannels; ++c) {
     if (algo == Algo::Ring) {
       for (const auto& blocks : ring_loops(chans[c], topo.nranks, chunk_count, unit))
-        for (int k = 0; k < topo.nranks; ++k) push(blocks[k].offset, blocks[k].count, (uint32_t)k);
+        for (int k = 0; k < topo.nranks; ++k) push(blocks[k].offset, blocks[k].count, orders.base[c] + (uint32_t)k);
     } else {
-      push(chans[c].offset, chans[c].count, (uint32_t)topo.channels[c].tree_index);
+      push(chans[c].offset, chans[c].count, orders.base[c]);
     }
   }
   // Cut at global multiples of the tile size, so that full tiles start on a
@@ -94,6 +94,58 @@ void build_fused_tiles(const Topology& topo, Algo algo, uint64_t count, uint64_t
       pos = next;
     }
   }
+}
+
+int build_fused_orders(const Topology& topo, Algo algo, FusedOrders* out) {
+  const int n = topo.nranks;
+  FusedOrders o;
+  o.base.assign(topo.nchannels, 0);
+  for (int j = 0; j < kMaxRanks; ++j) o.rotate_perm[j] = (uint8_t)(j < n ? j : 0);
+  if (algo == Algo::Ring) {
+    // Ring block k of channel c folds the ranks order[k], order[k+1], ...
+    if (topo.nrings == 1) {
+      o.mode = kRotate;
+      for (int j = 0; j < n; ++j) o.rotate_perm[j] = (uint8_t)topo.channels[0].order[j];
+    } else {
+      o.mode = kFold;
+      o.rows.assign((size_t)topo.nrings * kRowLen, 0);
+      for (const ChannelTopology& ch : topo.channels) {
+        uint32_t* row = &o.rows[(size_t)ch.ring_id * kRowLen];
+        for (int j = 0; j < 2 * n; ++j) row[j] = (uint32_t)ch.order[j % n];
+      }
+      for (int c = 0; c < topo.nchannels; ++c) o.base[c] = (uint32_t)topo.channels[c].ring_id << 8;
+    }
+    *out = std::move(o);
+    return EMU_SUCCESS;
+  }
+  // Tree: one program per distinct record set.
+  std::vector<uint8_t> perm((size_t)topo.ntrees * kMaxRanks), instr((size_t)topo.ntrees * kMaxRanks);
+  std::vector<bool> done(topo.ntrees, false);
+  bool all_pure = true;
+  for (const ChannelTopology& ch : topo.channels) {
+    if (done[ch.tree_id]) continue;
+    done[ch.tree_id] = true;
+    int nregs = 0;
+    bool pure = false;
+    if (int e = compile_tree_program(ch, &perm[(size_t)ch.tree_id * kMaxRanks],
+                                     &instr[(size_t)ch.tree_id * kMaxRanks], &nregs, &pure))
+      return e;
+    all_pure = all_pure && pure;
+  }
+  if (topo.ntrees == 1 && all_pure) {
+    o.mode = kRotate;   // one chain: a left fold over the permuted pointers, variant 0
+    for (int j = 0; j < n; ++j) o.rotate_perm[j] = perm[j];
+  } else {
+    o.mode = all_pure ? kFold : kProgram;
+    o.rows.assign((size_t)topo.ntrees * kRowLen, 0);
+    for (int t = 0; t < topo.ntrees; ++t)
+      for (int j = 0; j < n; ++j)
+        o.rows[(size_t)t * kRowLen + j] =
+            (uint32_t)perm[(size_t)t * kMaxRanks + j] | (uint32_t)instr[(size_t)t * kMaxRanks + j] << 8;
+    for (int c = 0; c < topo.nchannels; ++c) o.base[c] = (uint32_t)topo.channels[c].tree_id << 8;
+  }
+  *out = std::move(o);
+  return EMU_SUCCESS;
 }
 
 // ---------------------------------------------------------------------------
@@ -223,11 +275,17 @@ int compile_tree_program(const ChannelTopology& ch, uint8_t perm[kMaxRanks],
 
 void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,
                       uint64_t slice_elems, std::vector<RingLoopBlock>* loops,
-                      std::vector<RingTask>* tasks) {
+                      std::vector<RingTask>* tasks, std::vector<uint8_t>* orders) {
   loops->clear();
   tasks->clear();
+  orders->assign((size_t)topo.nrings * kMaxRanks, 0);
+  for (const ChannelTopology& c : topo.channels)
+    for (int p = 0; p < topo.nranks; ++p) (*orders)[(size_t)c.ring_id * kMaxRanks + p] = (uint8_t)c.order[p];
   uint32_t loop_id = 0;
-  for (const Range& ch : channel_ranges(count, unit, topo.nchannels)) {
+  const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
+  for (int c = 0; c < topo.nchannels; ++c) {
+    const Range& ch = chans[c];
+    const uint32_t ring = (uint32_t)topo.channels[c].ring_id;
     for (const auto& blocks : ring_loops(ch, topo.nranks, chunk_count, unit)) {
       // slices of a block = the slice-size cells of the global grid it overlaps
       uint64_t nslices = 0;
@@ -236,7 +294,7 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
         if (b.count)
           nslices = std::max(nslices, ceil_div(b.offset + b.count, slice_elems) - b.offset / slice_elems);
       }
-      for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q});
+      for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q, ring, 0});
       ++loop_id;
     }
   }
@@ -247,8 +305,8 @@ void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
                       std::vector<TreeNode>* nodes) {
   tasks->clear();
   const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
-  // Channels that use the same node-level tree are contiguous ranges of the
-  // message with identical per-element orders; each such segment is one
+  // Adjacent channels with the same tree records are contiguous ranges of
+  // the message with identical per-element orders; each such segment is one
   // stream of slices.  It is cut, at slice-cell boundaries, into pieces of
   // nearly equal size, one pipeline per workgroup, so that the pipeline's
   // fill and drain are paid once per piece rather than once per chunk
@@ -257,7 +315,7 @@ void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
   std::vector<Seg> segs;
   for (int c = 0; c < topo.nchannels; ++c) {
     if (chans[c].count == 0) continue;
-    if (!segs.empty() && topo.channels[segs.back().channel].tree_index == topo.channels[c].tree_index &&
+    if (!segs.empty() && topo.channels[segs.back().channel].tree_id == topo.channels[c].tree_id &&
         segs.back().end == chans[c].offset)
       segs.back().end = chans[c].offset + chans[c].count;
     else

@@ -25,24 +25,37 @@ std::vector<Range> tree_chunks(const Range& ch, uint64_t chunk_count);
 std::vector<std::vector<Range>> ring_loops(const Range& ch, int nranks, uint64_t chunk_count,
                                            uint64_t unit);
 
-// Fused mode: tiles of at most tile_elems elements, each inside one variant
-// segment (ring: one rank-chunk; tree: one node-level tree).
-void build_fused_tiles(const Topology& topo, Algo algo, uint64_t count, uint64_t unit,
-                       uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out);
-
-// Fused tree program for one channel tree (see TreeProgram in common.h).
+// Fused tree program for one channel tree (the kProgram encoding of
+// common.h: input order perm, per-input register instruction instr).
 // Returns EMU_SUCCESS or EMU_ERR_INTERNAL (register stack too deep, or the
 // self-check of the program against the fold definition failed).
 int compile_tree_program(const ChannelTopology& ch, uint8_t perm[kMaxRanks],
                          uint8_t instr[kMaxRanks], int* nregs, bool* pure_fold);
 
-// Stepwise ring: loop table (nranks blocks per loop) and tasks (loop, slice).
+// Fused orders of a communicator: the mode, the order rows, the pointer
+// permutation of kRotate, and each channel's variant base (the tile variant
+// of ring block k in channel c is base[c] + k; of a tree tile, base[c]).
+struct FusedOrders {
+  int mode = kRotate;
+  std::vector<uint32_t> rows;               // [nrows][kRowLen]
+  uint8_t rotate_perm[kMaxRanks] = {};      // kRotate: pointer j is rank rotate_perm[j]
+  std::vector<uint32_t> base;               // per channel
+};
+int build_fused_orders(const Topology& topo, Algo algo, FusedOrders* out);
+
+// Fused mode: tiles of at most tile_elems elements, each inside one variant
+// segment (ring: one rank-chunk of one ring order; tree: one tree).
+void build_fused_tiles(const Topology& topo, Algo algo, const FusedOrders& orders, uint64_t count,
+                       uint64_t unit, uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out);
+
+// Stepwise ring: loop table (nranks blocks per loop), tasks (loop, slice,
+// ring order) and the ring order table ([nrings][kMaxRanks]).
 void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,
                       uint64_t slice_elems, std::vector<RingLoopBlock>* loops,
-                      std::vector<RingTask>* tasks);
+                      std::vector<RingTask>* tasks, std::vector<uint8_t>* orders);
 
 // Stepwise tree: about target_tasks contiguous pieces of the message, each
-// inside one run of channels that share a node-level tree and cut at
+// inside one run of channels with the same tree records and cut at
 // slice-cell boundaries, and the per-(channel, rank) tree table.
 void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t slice_elems,
                       uint64_t target_tasks, std::vector<TreeTask>* tasks,

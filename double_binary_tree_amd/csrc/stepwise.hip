@@ -12,9 +12,11 @@
 //
 // Ring (page "all-reduce 每张卡要发多少数据? ring 和 tree 有什么区别?", Figure 1
 // and section "手撕代码"; page "NCCL 内部机制：…", section "Ring：带宽友好…"):
-//   step 0: rank r sends its block r;  steps 1..N-1: rank r receives block
-//   (r-s) mod N, adds its own input, sends it on (the last of these writes
-//   the finished block); then N-1 all-gather steps forward finished blocks.
+//   lane group p is ring position p, played by the rank the channel's order
+//   puts there.  step 0: position p sends its block p;  steps 1..N-1: it
+//   receives block (p-s) mod N, adds its own input, sends it on (the last
+//   of these writes the finished block); then N-1 all-gather steps forward
+//   finished blocks.
 // Tree (page "NCCL 专家课程 13", sections "runTreeSplit 如何流水" and "每种
 // rank 的操作"): a rank at depth d reduces slice q at stage q + (H - d)
 // (children's partials arrive from the previous stage) and, if not the root,
@@ -57,9 +59,9 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_RING_VPT;
   constexpr int kPrefetch = EMU_RING_PREFETCH;
-  extern __shared__ u32x4 fifo[];   // slots [2][N][V][G], then descriptors [2][N]
+  extern __shared__ u32x4 fifo[];   // slots [2][N][V][G], descriptors [2][N], ring orders [2][kMaxRanks] bytes
   const uint32_t n = a.nranks, g = a.group;
-  const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;
+  const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;   // r: ring position
   const bool active = r < n;
   const uint32_t prev = active ? (r + n - 1) % n : 0;
   const RingLoopBlock* loops = static_cast<const RingLoopBlock*>(a.table);
@@ -71,9 +73,13 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   // sets) so that no step waits on a descriptor load: the next task's are
   // copied during the current task's first step.
   RingLoopBlock* desc = reinterpret_cast<RingLoopBlock*>(fifo + 2 * (size_t)n * V * g);   // [2][N]
+  uint8_t* order = reinterpret_cast<uint8_t*>(desc + 2 * n);                                // [2][kMaxRanks]
   auto stage_desc = [&](uint32_t t, uint32_t set) {
-    if (t < a.ntasks && threadIdx.x < n)
-      desc[set * n + threadIdx.x] = loops[(size_t)tasks[t].loop * n + threadIdx.x];
+    if (t < a.ntasks && threadIdx.x < n) {
+      const RingTask tk = tasks[t];
+      desc[set * n + threadIdx.x] = loops[(size_t)tk.loop * n + threadIdx.x];
+      order[set * kMaxRanks + threadIdx.x] = a.orders[(size_t)tk.ring * kMaxRanks + threadIdx.x];
+    }
   };
   stage_desc(blockIdx.x, 0);
   step_barrier();
@@ -82,6 +88,7 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x, set ^= 1) {
     const RingTask task = tasks[t];
     const RingLoopBlock* blk = desc + set * n;
+    const uint32_t me = active ? order[set * kMaxRanks + r] : 0;   // the rank at position r
     if (n > 1) stage_desc(t + gridDim.x, set ^ 1);   // visible after this task's barriers
     // Slice q of block b is the q-th slice-size cell of the global element
     // grid that the block overlaps; lane p's vector v sits at a fixed place in
@@ -101,14 +108,14 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int nb = nbytes_of(b, v);
-        x[v] = nb ? ld_any(a.send[r], boff_of(b, v), nb) : u32x4{0, 0, 0, 0};
+        x[v] = nb ? ld_any(a.send[me], boff_of(b, v), nb) : u32x4{0, 0, 0, 0};
       }
     };
     auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int nb = nbytes_of(b, v);
-        if (nb) st_any(a.recv[r], boff_of(b, v), nb, R::post(x[v]));
+        if (nb) st_any(a.recv[me], boff_of(b, v), nb, R::post(x[v]));
       }
     };
 

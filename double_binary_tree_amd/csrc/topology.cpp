@@ -1,6 +1,8 @@
 // Host topology builder.  Sources: page "NCCL 专家课程 13：Tree、双树、层次化
 // 连接与真实交叉区间", sections "Btree 的 bit 构造", "双树：偶数 mirror，奇数
-// shift", "节点内先形成链", "节点间连接", "从 GRAPH 日志复原 active tree".
+// shift", "节点内先形成链" (chain order and head pattern), "节点间连接",
+// "从 GRAPH 日志复原 active tree"; page "NCCL代码分析", section "Tree搜索"
+// (the three intra-node tree patterns).
 #include "topology.h"
 
 #include <cstdio>
@@ -95,15 +97,41 @@ bool check_channel(const ChannelTopology& ch) {
   return true;
 }
 
-int build_topology(int nranks, int nnodes, int nchannels, Topology* out) {
+// Chain positions of the parent, child0 and child1 heads of a node.
+static bool head_positions(int pattern, int pos[3]) {
+  switch (pattern) {
+    case EMU_PATTERN_TREE: pos[0] = 0; pos[1] = 0; pos[2] = 0; return true;
+    case EMU_PATTERN_SPLIT_TREE: pos[0] = 0; pos[1] = 1; pos[2] = 1; return true;
+    case EMU_PATTERN_BALANCED_TREE: pos[0] = 0; pos[1] = 1; pos[2] = 0; return true;
+    default: return false;
+  }
+}
+
+int build_topology(int nranks, int nnodes, int nchannels, int pattern, const int* intra, Topology* out) {
   if (nranks < 1 || nranks > kMaxRanks || nnodes < 1 || nranks % nnodes != 0 ||
       nchannels < 1 || nchannels > kMaxChannels)
     return EMU_ERR_INVALID_ARGUMENT;
+  const int L = nranks / nnodes;
+  int pos[3];
+  if (!head_positions(pattern, pos)) return EMU_ERR_INVALID_ARGUMENT;
+  if (pos[1] >= L || pos[2] >= L) return EMU_ERR_INVALID_ARGUMENT;
+  if (intra) {
+    // every node's part of every row is a permutation of that node's ranks
+    for (int c = 0; c < nchannels; ++c)
+      for (int node = 0; node < nnodes; ++node) {
+        uint64_t seen = 0;
+        for (int i = 0; i < L; ++i) {
+          const int r = intra[(size_t)c * nranks + node * L + i];
+          if (r < node * L || r >= (node + 1) * L || (seen >> (r - node * L) & 1)) return EMU_ERR_INVALID_ARGUMENT;
+          seen |= (uint64_t)1 << (r - node * L);
+        }
+      }
+  }
   Topology topo;
   topo.nranks = nranks;
   topo.nnodes = nnodes;
   topo.nchannels = nchannels;
-  const int L = nranks / nnodes;
+  topo.pattern = pattern;
   topo.depth_approx = L - 1 + log2_floor(nnodes);
   std::vector<std::array<NodeTreeEdges, 2>> node_trees(nnodes);
   for (int m = 0; m < nnodes; ++m) node_trees[m] = node_dtree(nnodes, m);
@@ -111,22 +139,26 @@ int build_topology(int nranks, int nnodes, int nchannels, Topology* out) {
   for (int c = 0; c < nchannels; ++c) {
     ChannelTopology ch;
     ch.tree_index = c < first_half ? 0 : 1;
+    ch.order.resize(nranks);
+    for (int i = 0; i < nranks; ++i) ch.order[i] = intra ? intra[(size_t)c * nranks + i] : i;
     ch.ranks.assign(nranks, RankRecord{});
-    // chain inside every node, identity order
+    // chain inside every node, in the channel's order
+    auto at = [&](int node, int i) { return ch.order[node * L + i]; };
     for (int node = 0; node < nnodes; ++node) {
       for (int i = 0; i < L; ++i) {
-        const int r = node * L + i;
-        ch.ranks[r].up = i > 0 ? r - 1 : -1;
-        ch.ranks[r].down[0] = i < L - 1 ? r + 1 : -1;
+        const int r = at(node, i);
+        ch.ranks[r].up = i > 0 ? at(node, i - 1) : -1;
+        ch.ranks[r].down[0] = i < L - 1 ? at(node, i + 1) : -1;
       }
     }
-    // node-level edges on the heads (local index 0): parent, child0, child1
+    // node-level edges between heads: a node's parent head goes up to the
+    // parent node's child0 or child1 head (by child type); a child head
+    // takes the child node's parent head, child0 before child1.
     for (int node = 0; node < nnodes; ++node) {
-      const int head = node * L;
       const NodeTreeEdges& e = node_trees[node][ch.tree_index];
-      if (e.parent != -1) ch.ranks[head].up = e.parent * L;
-      if (!attach_down(ch.ranks[head], e.child0 < 0 ? -1 : e.child0 * L)) return EMU_ERR_INTERNAL;
-      if (!attach_down(ch.ranks[head], e.child1 < 0 ? -1 : e.child1 * L)) return EMU_ERR_INTERNAL;
+      if (e.parent != -1) ch.ranks[at(node, pos[0])].up = at(e.parent, pos[1 + e.child_type]);
+      if (e.child0 != -1 && !attach_down(ch.ranks[at(node, pos[1])], at(e.child0, pos[0]))) return EMU_ERR_INTERNAL;
+      if (e.child1 != -1 && !attach_down(ch.ranks[at(node, pos[2])], at(e.child1, pos[0]))) return EMU_ERR_INTERNAL;
     }
     if (!check_channel(ch)) return EMU_ERR_INTERNAL;
     ch.depth.assign(nranks, 0);
@@ -138,6 +170,22 @@ int build_topology(int nranks, int nnodes, int nchannels, Topology* out) {
       if (d > ch.height) ch.height = d;
       if (d == 0) ch.root = r;
     }
+    // ids of the distinct orders and record sets seen so far
+    ch.ring_id = topo.nrings;
+    ch.tree_id = topo.ntrees;
+    for (const ChannelTopology& o : topo.channels) {
+      if (o.order == ch.order) { ch.ring_id = o.ring_id; break; }
+    }
+    for (const ChannelTopology& o : topo.channels) {
+      bool same = true;
+      for (int r = 0; r < nranks && same; ++r) {
+        const RankRecord &a = o.ranks[r], &b = ch.ranks[r];
+        same = a.up == b.up && a.down[0] == b.down[0] && a.down[1] == b.down[1] && a.down[2] == b.down[2];
+      }
+      if (same) { ch.tree_id = o.tree_id; break; }
+    }
+    if (ch.ring_id == topo.nrings) ++topo.nrings;
+    if (ch.tree_id == topo.ntrees) ++topo.ntrees;
     topo.channels.push_back(std::move(ch));
   }
   if (const char* dbg = std::getenv("EMU_DEBUG")) {

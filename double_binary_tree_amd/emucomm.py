@@ -44,6 +44,9 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.emu_comm_init.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t]
         L.emu_comm_init.restype = ctypes.c_int
+        L.emu_comm_init_graph.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_size_t,
+                                          ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.emu_comm_init_graph.restype = ctypes.c_int
         L.emu_allreduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                     ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.emu_allreduce.restype = ctypes.c_int
@@ -77,9 +80,33 @@ def comm_init_raw(nranks: int, nnodes: int, algo: int, nchannels: int, chunk_byt
     return lib().emu_comm_init(nranks, nnodes, algo, nchannels, chunk_bytes)
 
 
+PATTERNS = {"tree": 0, "split": 1, "balanced": 2}
+
+
+def comm_init_graph_raw(nranks: int, nnodes: int, algo: int, nchannels: int, chunk_bytes: int,
+                        pattern: int, intra=None) -> int:
+    """emu_comm_init_graph; ``intra`` is None or nchannels rows of nranks ranks."""
+    arr = None
+    if intra is not None:
+        flat = [int(r) for row in intra for r in row]
+        arr = (ctypes.c_int * len(flat))(*flat)
+    return lib().emu_comm_init_graph(nranks, nnodes, algo, nchannels, chunk_bytes, pattern, arr)
+
+
 def comm_init(nranks: int, nnodes: int, algo: str, nchannels: int, chunk_bytes: int,
-              mode: str = "stepwise") -> None:
-    _check(comm_init_raw(nranks, nnodes, algo_code(algo, mode), nchannels, chunk_bytes), "emu_comm_init")
+              mode: str = "stepwise", pattern: str = "tree", intra=None) -> None:
+    """Build the communicator.  ``pattern`` ("tree", "split", "balanced") and
+    ``intra`` (per-channel rank orders, node after node) select the graph;
+    the defaults are the plain emu_comm_init."""
+    if pattern == "tree" and intra is None:
+        _check(comm_init_raw(nranks, nnodes, algo_code(algo, mode), nchannels, chunk_bytes), "emu_comm_init")
+        return
+    if pattern not in PATTERNS:
+        raise ValueError(f"unknown pattern {pattern!r}")
+    if intra is not None and (len(intra) != nchannels or any(len(row) != nranks for row in intra)):
+        raise ValueError("intra needs nchannels rows of nranks ranks")
+    _check(comm_init_graph_raw(nranks, nnodes, algo_code(algo, mode), nchannels, chunk_bytes,
+                               PATTERNS[pattern], intra), "emu_comm_init_graph")
 
 
 def allreduce_raw(sendptrs, recvptrs, count: int, dtype: int, op: int, stream: int = 0) -> int:

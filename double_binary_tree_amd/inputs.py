@@ -118,3 +118,14 @@ def rank_inputs(w: Workload, count: int | None = None, salt: int = 0) -> list[np
     seed = SEED_BASE + w.seed_index + 1000 * salt
     children = np.random.SeedSequence(seed).spawn(w.nranks)
     return [draw(np.random.Generator(np.random.PCG64(ch)), w.dtype, w.dist, n) for ch in children]
+
+
+def intra_orders(nranks: int, nnodes: int, nchannels: int, seed: int, distinct: int = 3) -> list[list[int]]:
+    """Seeded per-channel rank orders for graph test cases: each channel takes
+    one of ``distinct`` random orders, each a permutation of every node's
+    ranks, node after node (rank = node * L + local)."""
+    rng = np.random.default_rng(SEED_BASE + seed)
+    L = nranks // nnodes
+    pool = [[int(r) for m in range(nnodes) for r in rng.permutation(range(m * L, (m + 1) * L))]
+            for _ in range(distinct)]
+    return [pool[int(rng.integers(0, distinct))] for _ in range(nchannels)]

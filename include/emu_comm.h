@@ -31,7 +31,8 @@ extern "C" {
 
 /* Algorithms (low byte of `algo`).  TREE on one node is the intra-node
  * chain; on several nodes it is the chain inside each node plus the double
- * binary tree across node heads (local rank 0 of every node). */
+ * binary tree across node heads (by default local rank 0 of every node; see
+ * emu_comm_init_graph for other chain orders and head patterns). */
 #define EMU_ALGO_RING 0
 #define EMU_ALGO_TREE 1
 /* Execution mode, OR-ed into `algo`.
@@ -65,6 +66,18 @@ extern "C" {
 #define EMU_ERR_INTERNAL 3
 #define EMU_ERR_HIP 4
 
+/* Intra-node head patterns (page "NCCL 专家课程 13", section "节点内先形成
+ * 链"; page "NCCL代码分析", section "Tree搜索"): which chain positions of a
+ * node carry its node-level edges.  The edge to the parent node always
+ * leaves from chain position 0; the edges from the child nodes arrive at
+ *   TREE           position 0 (child0 and child1),
+ *   SPLIT_TREE     position 1 (child0 and child1),
+ *   BALANCED_TREE  position 1 (child0) and position 0 (child1).
+ * SPLIT_TREE and BALANCED_TREE need at least two ranks per node. */
+#define EMU_PATTERN_TREE 0
+#define EMU_PATTERN_SPLIT_TREE 1
+#define EMU_PATTERN_BALANCED_TREE 2
+
 /* Limits. */
 #define EMU_MAX_RANKS 64
 #define EMU_MAX_CHANNELS 64
@@ -95,6 +108,29 @@ extern "C" {
  * within the limits above).
  */
 int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes);
+
+/*
+ * emu_comm_init_graph - emu_comm_init with per-channel rank orders and a head
+ * pattern, the two things a graph search hands to the tree and ring builders
+ * (page "NCCL 专家课程 13", section "节点内先形成链", and the per-channel
+ * chain table of section "从 GRAPH 日志复原 active tree").
+ *   pattern  EMU_PATTERN_TREE, EMU_PATTERN_SPLIT_TREE or
+ *            EMU_PATTERN_BALANCED_TREE
+ *   intra    NULL (every channel in identity order), or nchannels * nranks
+ *            ints: row c lists node 0's ranks in channel c's chain order,
+ *            then node 1's, and so on; each node's part is a permutation of
+ *            that node's ranks.  Tree: the chain inside each node follows
+ *            the order (parent = previous, first child = next).  Ring: the
+ *            ring of channel c visits the ranks in the row's order, node
+ *            after node.  Read during the call only.
+ * The other arguments, the caching and the errors are those of
+ * emu_comm_init; EMU_ERR_INVALID_ARGUMENT also for an unknown pattern, a
+ * pattern that needs two ranks per node on one-rank nodes, or a row that is
+ * not a node-by-node permutation.  emu_comm_init(...) is
+ * emu_comm_init_graph(..., EMU_PATTERN_TREE, NULL).
+ */
+int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes,
+                        int pattern, const int* intra);
 
 /*
  * emu_allreduce - enqueue one all-reduce on `stream` (a hipStream_t; NULL is

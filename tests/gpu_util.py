@@ -39,11 +39,11 @@ def to_host_bits(t, dtype: str) -> np.ndarray:
 
 
 def run_allreduce(inputs, nnodes, algo, mode, nchannels, chunk_bytes, dtype, op, inplace=False,
-                  sends=None):
+                  sends=None, pattern="tree", intra=None):
     """Run one all-reduce through the C ABI; returns (outputs as numpy, send tensors)."""
     import torch
     n = len(inputs)
-    E.comm_init(n, nnodes, algo, nchannels, chunk_bytes, mode=mode)
+    E.comm_init(n, nnodes, algo, nchannels, chunk_bytes, mode=mode, pattern=pattern, intra=intra)
     if sends is None:
         sends = [to_device(x, dtype) for x in inputs]
     if inplace:

@@ -2,9 +2,13 @@
 // stdout, for tests/test_host_planner.py to check against the oracle.
 // Built with plain g++ (and sanitizers) from the host-only planner sources.
 //
-// usage: planner_dump nranks nnodes nchannels chunk_bytes esz count
+// usage: planner_dump nranks nnodes nchannels chunk_bytes esz count pattern intra
+//   pattern  0 tree, 1 split, 2 balanced
+//   intra    "-" for identity orders, else nchannels*nranks comma-separated ranks
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <string>
 #include <vector>
 
 #include "../../double_binary_tree_amd/csrc/plan.h"
@@ -12,44 +16,81 @@
 
 using namespace emu;
 
+static void print_orders(const char* name, const FusedOrders& o, const std::vector<Tile>& tiles) {
+  std::printf("\"%s\": {\"mode\": %d, \"rotate_perm\": [", name, o.mode);
+  for (int j = 0; j < kMaxRanks; ++j) std::printf("%s%u", j ? "," : "", o.rotate_perm[j]);
+  std::printf("], \"rows\": [");
+  for (size_t i = 0; i < o.rows.size(); ++i) std::printf("%s%u", i ? "," : "", o.rows[i]);
+  std::printf("], \"base\": [");
+  for (size_t i = 0; i < o.base.size(); ++i) std::printf("%s%u", i ? "," : "", o.base[i]);
+  std::printf("], \"tiles\": [");
+  for (size_t i = 0; i < tiles.size(); ++i)
+    std::printf("%s[%llu,%u,%u]", i ? "," : "", (unsigned long long)tiles[i].start, tiles[i].nelem,
+                tiles[i].variant);
+  std::printf("]},");
+}
+
 int main(int argc, char** argv) {
-  if (argc != 7) {
-    std::fprintf(stderr, "usage: %s nranks nnodes nchannels chunk_bytes esz count\n", argv[0]);
+  if (argc != 9) {
+    std::fprintf(stderr, "usage: %s nranks nnodes nchannels chunk_bytes esz count pattern intra\n", argv[0]);
     return 2;
   }
   const int n = std::atoi(argv[1]), m = std::atoi(argv[2]), nch = std::atoi(argv[3]);
   const uint64_t chunk_bytes = std::strtoull(argv[4], nullptr, 10);
   const int esz = std::atoi(argv[5]);
   const uint64_t count = std::strtoull(argv[6], nullptr, 10);
+  const int pattern = std::atoi(argv[7]);
+  std::vector<int> intra;
+  if (std::strcmp(argv[8], "-") != 0) {
+    for (const char* p = argv[8]; *p;) {
+      char* end = nullptr;
+      intra.push_back((int)std::strtol(p, &end, 10));
+      p = (*end == ',') ? end + 1 : end;
+    }
+    if (intra.size() != (size_t)n * nch) {
+      std::fprintf(stderr, "intra needs %d entries\n", n * nch);
+      return 2;
+    }
+  }
   const uint64_t unit = 16 / esz, chunk = chunk_bytes / esz;
   Topology topo;
-  if (int e = build_topology(n, m, nch, &topo)) {
+  if (int e = build_topology(n, m, nch, pattern, intra.empty() ? nullptr : intra.data(), &topo)) {
     std::printf("{\"error\": %d}\n", e);
     return 0;
   }
-  std::printf("{");
-  // fused tiles, both algorithms, tile of 256 vectors
+  std::printf("{\"nrings\": %d, \"ntrees\": %d, \"ring_id\": [", topo.nrings, topo.ntrees);
+  for (int c = 0; c < nch; ++c) std::printf("%s%d", c ? "," : "", topo.channels[c].ring_id);
+  std::printf("], \"tree_id\": [");
+  for (int c = 0; c < nch; ++c) std::printf("%s%d", c ? "," : "", topo.channels[c].tree_id);
+  std::printf("],");
+  // fused orders and tiles, both algorithms, tile of 256 vectors
   for (int algo = 0; algo < 2; ++algo) {
+    const Algo a = algo == 0 ? Algo::Ring : Algo::Tree;
+    FusedOrders orders;
+    if (int e = build_fused_orders(topo, a, &orders)) {
+      std::printf("\"fused_%s\": {\"error\": %d},", algo == 0 ? "ring" : "tree", e);
+      continue;
+    }
     std::vector<Tile> tiles;
-    build_fused_tiles(topo, algo == 0 ? Algo::Ring : Algo::Tree, count, unit, chunk, 256 * unit, &tiles);
-    std::printf("\"tiles_%s\": [", algo == 0 ? "ring" : "tree");
-    for (size_t i = 0; i < tiles.size(); ++i)
-      std::printf("%s[%llu,%u,%u]", i ? "," : "", (unsigned long long)tiles[i].start, tiles[i].nelem,
-                  tiles[i].variant);
-    std::printf("],");
+    build_fused_tiles(topo, a, orders, count, unit, chunk, 256 * unit, &tiles);
+    print_orders(algo == 0 ? "fused_ring" : "fused_tree", orders, tiles);
   }
   // stepwise ring loop table and tasks, slice of 64 lanes x 1 vector
   {
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
+    std::vector<uint8_t> orders;
     const uint64_t slice = 64 * unit;
-    build_ring_tasks(topo, count, unit, chunk, slice, &loops, &tasks);
+    build_ring_tasks(topo, count, unit, chunk, slice, &loops, &tasks, &orders);
     std::printf("\"ring_slice\": %llu, \"ring_blocks\": [", (unsigned long long)slice);
     for (size_t i = 0; i < loops.size(); ++i)
       std::printf("%s[%llu,%u,%u]", i ? "," : "", (unsigned long long)loops[i].offset, loops[i].nelem,
                   loops[i].first_cell);
     std::printf("], \"ring_tasks\": [");
-    for (size_t i = 0; i < tasks.size(); ++i) std::printf("%s[%u,%u]", i ? "," : "", tasks[i].loop, tasks[i].slice);
+    for (size_t i = 0; i < tasks.size(); ++i)
+      std::printf("%s[%u,%u,%u]", i ? "," : "", tasks[i].loop, tasks[i].slice, tasks[i].ring);
+    std::printf("], \"ring_orders\": [");
+    for (size_t i = 0; i < orders.size(); ++i) std::printf("%s%u", i ? "," : "", orders[i]);
     std::printf("],");
   }
   // stepwise tree tasks
@@ -68,18 +109,15 @@ int main(int argc, char** argv) {
                   nodes[i].down[2], nodes[i].depth);
     std::printf("],");
   }
-  // fused tree programs of tree 0 and tree 1
+  // compiled tree program of every channel
   std::printf("\"programs\": [");
-  for (int t = 0; t < 2; ++t) {
-    const ChannelTopology* ch = &topo.channels[0];
-    for (const auto& c : topo.channels)
-      if (c.tree_index == t) { ch = &c; break; }
+  for (int c = 0; c < nch; ++c) {
     uint8_t perm[kMaxRanks], instr[kMaxRanks];
     int nregs = 0;
     bool pure = false;
-    const int e = compile_tree_program(*ch, perm, instr, &nregs, &pure);
-    std::printf("%s{\"tree\": %d, \"error\": %d, \"nregs\": %d, \"pure\": %d, \"perm\": [", t ? "," : "", ch->tree_index,
-                e, nregs, pure ? 1 : 0);
+    const int e = compile_tree_program(topo.channels[c], perm, instr, &nregs, &pure);
+    std::printf("%s{\"channel\": %d, \"error\": %d, \"nregs\": %d, \"pure\": %d, \"perm\": [", c ? "," : "", c, e,
+                nregs, pure ? 1 : 0);
     for (int i = 0; i < n; ++i) std::printf("%s%u", i ? "," : "", perm[i]);
     std::printf("], \"instr\": [");
     for (int i = 0; i < n; ++i) std::printf("%s%u", i ? "," : "", instr[i]);

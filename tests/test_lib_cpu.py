@@ -71,6 +71,64 @@ def test_ring_comm_also_reports_topology():
     assert E.tree_topology(11, 7) == (6, [-1, -1, -1])
 
 
+def _orders(rng, n, m, nch):
+    L = n // m
+    return [[int(r) for node in range(m) for r in rng.permutation(range(node * L, (node + 1) * L))]
+            for _ in range(nch)]
+
+
+@pytest.mark.parametrize("pattern", ["tree", "split", "balanced"])
+def test_graph_topology_matches_oracle(pattern):
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for n, m, nch in ((4, 2, 2), (6, 3, 4), (8, 2, 5), (12, 4, 3), (32, 4, 16), (64, 8, 8), (30, 5, 6),
+                      (18, 9, 2), (4, 1, 12), (3, 1, 2)):
+        for intra in (None, _orders(rng, n, m, nch)):
+            E.comm_init(n, m, "tree", nch, 1 << 19, pattern=pattern, intra=intra)
+            ref = T.build_topology(n, m, nch, pattern, intra)
+            for c in range(nch):
+                for r in range(n):
+                    assert E.tree_topology(c, r) == (ref.channels[c].up[r], ref.channels[c].down[r]), \
+                        (pattern, n, m, c, r)
+
+
+def test_graph_table_chains():
+    # The per-channel chains of the pages' 4-GPU table (12 channels, 3 orders).
+    order = {0: [0, 1, 2, 3], 1: [0, 1, 2, 3], 6: [0, 1, 2, 3], 7: [0, 1, 2, 3],
+             2: [0, 2, 1, 3], 3: [0, 2, 1, 3], 8: [0, 2, 1, 3], 9: [0, 2, 1, 3],
+             4: [1, 0, 3, 2], 5: [1, 0, 3, 2], 10: [1, 0, 3, 2], 11: [1, 0, 3, 2]}
+    intra = [order[c] for c in range(12)]
+    E.comm_init(4, 1, "tree", 12, 1 << 19, mode="fused", intra=intra)
+    for c in range(12):
+        o = order[c]
+        for i, r in enumerate(o):
+            up, down = E.tree_topology(c, r)
+            assert up == (o[i - 1] if i else -1)
+            assert down == [o[i + 1] if i < 3 else -1, -1, -1]
+
+
+def test_init_graph_rejects_bad_graphs_and_keeps_state():
+    E.comm_init(4, 2, "tree", 2, 1 << 19)
+    raw = E.comm_init_graph_raw
+    assert raw(4, 4, 1, 2, 1 << 19, 1) == E.ERR_INVALID_ARGUMENT          # split, one rank per node
+    assert raw(4, 4, 1, 2, 1 << 19, 2) == E.ERR_INVALID_ARGUMENT          # balanced, one rank per node
+    assert raw(4, 1, 1, 1, 1 << 19, 3) == E.ERR_INVALID_ARGUMENT          # unknown pattern
+    assert raw(4, 1, 1, 1, 1 << 19, -1) == E.ERR_INVALID_ARGUMENT
+    assert raw(4, 2, 1, 1, 1 << 19, 0, [[0, 2, 1, 3]]) == E.ERR_INVALID_ARGUMENT   # rank 2 on node 1
+    assert raw(4, 1, 1, 1, 1 << 19, 0, [[0, 1, 1, 3]]) == E.ERR_INVALID_ARGUMENT   # repeated rank
+    assert raw(4, 1, 1, 1, 1 << 19, 0, [[0, 1, 2, 4]]) == E.ERR_INVALID_ARGUMENT   # out of range
+    assert raw(4, 1, 1, 1, 1 << 19, 0, [[0, 1, 2, -1]]) == E.ERR_INVALID_ARGUMENT
+    assert raw(4, 1, 7, 1, 1 << 19, 0) == E.ERR_INVALID_ARGUMENT          # algo
+    up, down = E.tree_topology(0, 2)
+    ref = T.build_topology(4, 2, 2).channels[0]
+    assert (up, down) == (ref.up[2], ref.down[2])
+    # the plain init is the graph init with the tree pattern and identity orders
+    assert raw(4, 2, 1, 2, 1 << 19, 0) == E.SUCCESS
+    assert (E.tree_topology(0, 2)) == (ref.up[2], ref.down[2])
+    with pytest.raises(ValueError):
+        E.comm_init(4, 1, "tree", 2, 1 << 19, intra=[[0, 1, 2, 3]])       # one row per channel
+
+
 def test_init_rejects_bad_arguments_and_keeps_state():
     E.comm_init(4, 2, "tree", 2, 1 << 19)
     bad = [

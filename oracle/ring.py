@@ -35,6 +35,44 @@ from __future__ import annotations
 from typing import Any, Callable
 
 
+def ring_reduce_scatter_steps(bufs: list[list[Any]], combine: Callable[[Any, Any], Any],
+                              copy: Callable[[Any], Any], trace: list | None = None,
+                              sent: list[int] | None = None, size: Callable[[Any], int] | None = None) -> None:
+    """The n-1 reduce-scatter steps, in place on ``bufs[r][b]`` (position r,
+    block b): at step s every position r sends block (r-s) mod n to r+1,
+    which adds it to its own copy of that block; all sends of a step read the
+    values from before the step.  Afterwards position r holds the full
+    reduction of block (r+1) mod n.  ``trace``/``sent``/``size`` as in
+    :func:`ring_allreduce_blocks`."""
+    n = len(bufs)
+    for s in range(n - 1):
+        outgoing = [copy(bufs[r][(r - s) % n]) for r in range(n)]
+        for r in range(n):
+            dst, b = (r + 1) % n, (r - s) % n
+            bufs[dst][b] = combine(bufs[dst][b], outgoing[r])
+            if sent is not None:
+                sent[r] += size(outgoing[r])
+        if trace is not None:
+            trace.append((("RS", s + 1), [[copy(b) for b in row] for row in bufs]))
+
+
+def ring_all_gather_steps(bufs: list[list[Any]], copy: Callable[[Any], Any], trace: list | None = None,
+                          sent: list[int] | None = None, size: Callable[[Any], int] | None = None) -> None:
+    """The n-1 all-gather steps, in place: position r starts with (at least)
+    block (r+1) mod n; at step s it sends block (r+1-s) mod n to r+1, which
+    overwrites its copy.  Afterwards every position holds every block."""
+    n = len(bufs)
+    for s in range(n - 1):
+        outgoing = [copy(bufs[r][(r + 1 - s) % n]) for r in range(n)]
+        for r in range(n):
+            dst, b = (r + 1) % n, (r + 1 - s) % n
+            bufs[dst][b] = outgoing[r]
+            if sent is not None:
+                sent[r] += size(outgoing[r])
+        if trace is not None:
+            trace.append((("AG", s + 1), [[copy(b) if b is not None else None for b in row] for row in bufs]))
+
+
 def ring_allreduce_blocks(bufs: list[list[Any]], combine: Callable[[Any, Any], Any],
                           copy: Callable[[Any], Any],
                           trace: list | None = None,
@@ -51,26 +89,5 @@ def ring_allreduce_blocks(bufs: list[list[Any]], combine: Callable[[Any, Any], A
     for r in range(n):
         if len(bufs[r]) != n:
             raise ValueError("every rank needs one block per rank")
-
-    def snapshot(label):
-        if trace is not None:
-            trace.append((label, [[copy(b) for b in row] for row in bufs]))
-
-    # reduce-scatter
-    for s in range(n - 1):
-        outgoing = [copy(bufs[r][(r - s) % n]) for r in range(n)]
-        for r in range(n):
-            dst, b = (r + 1) % n, (r - s) % n
-            bufs[dst][b] = combine(bufs[dst][b], outgoing[r])
-            if sent is not None:
-                sent[r] += size(outgoing[r])
-        snapshot(("RS", s + 1))
-    # all-gather
-    for s in range(n - 1):
-        outgoing = [copy(bufs[r][(r + 1 - s) % n]) for r in range(n)]
-        for r in range(n):
-            dst, b = (r + 1) % n, (r + 1 - s) % n
-            bufs[dst][b] = outgoing[r]
-            if sent is not None:
-                sent[r] += size(outgoing[r])
-        snapshot(("AG", s + 1))
+    ring_reduce_scatter_steps(bufs, combine, copy, trace, sent, size)
+    ring_all_gather_steps(bufs, copy, trace, sent, size)

@@ -18,10 +18,10 @@
 namespace emu {
 
 // Defined in fused.hip / stepwise.hip.
-hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows,
-                        int grid, hipStream_t stream);
+hipError_t launch_fused(Coll coll, DType t, Op op, int mode, const FusedArgs& a, const Tile* tiles,
+                        const uint32_t* rows, int grid, hipStream_t stream);
 int fused_tile_vectors();
-hipError_t launch_stepwise(bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
+hipError_t launch_stepwise(Coll coll, bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
                            size_t lds, hipStream_t s);
 int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds);
 int stepwise_vectors_per_lane(bool ring);
@@ -66,9 +66,10 @@ struct Comm {
   bool fused = false;
   size_t chunk_bytes = 0;
   Topology topo;
-  FusedOrders orders;   // fused mode: how each tile names its order
-  // (device, count, dtype, op) -> plan
-  std::map<std::tuple<int, uint64_t, int, int>, std::unique_ptr<Plan>> plans;
+  FusedOrders orders;        // fused all-reduce: how each tile names its order
+  FusedOrders ring_orders;   // fused reduce-scatter: the ring orders (any algo)
+  // (device, count, dtype, op, collective) -> plan
+  std::map<std::tuple<int, uint64_t, int, int, int>, std::unique_ptr<Plan>> plans;
 };
 
 using CommKey = std::tuple<int, int, int, int, size_t, int, std::vector<int>>;
@@ -99,7 +100,9 @@ int cu_count(int dev) {
   return cus;
 }
 
-int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
+// `count` is the elements per rank of the all-reduce, or the block size of
+// the reduce-scatter / all-gather.
+int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op, Plan* p) {
   const int esz = elem_size(t);
   const uint64_t unit = kVecBytes / esz;
   const uint64_t chunk_count = c.chunk_bytes / esz;
@@ -107,16 +110,20 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
   if (c.fused) {
     std::vector<Tile> tiles;
     const uint64_t tile_elems = (uint64_t)fused_tile_vectors() * unit;
-    build_fused_tiles(c.topo, c.algo, c.orders, count, unit, chunk_count, tile_elems, &tiles);
+    const FusedOrders& ord = coll == kAllReduce ? c.orders : c.ring_orders;
+    if (coll == kAllReduce)
+      build_fused_tiles(c.topo, c.algo, ord, count, unit, chunk_count, tile_elems, &tiles);
+    else
+      build_fused_coll_tiles(c.topo, coll, ord, count, unit, tile_elems, &tiles);
     p->ntiles = (uint32_t)tiles.size();
     if (int e = p->tiles.upload(tiles.data(), tiles.size() * sizeof(Tile))) return e;
-    if (int e = p->rows.upload(c.orders.rows.data(), c.orders.rows.size() * sizeof(uint32_t))) return e;
+    if (int e = p->rows.upload(ord.rows.data(), ord.rows.size() * sizeof(uint32_t))) return e;
     const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 64);
     p->fused_grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntiles, (uint64_t)cus * per_cu));
     return EMU_SUCCESS;
   }
   const int n = c.nranks;
-  const bool ring = c.algo == Algo::Ring;
+  const bool ring = c.algo == Algo::Ring || coll != kAllReduce;
   const int vpl = stepwise_vectors_per_lane(ring);
   // Lanes per virtual rank: the widest group that fits one workgroup
   // (N*G <= 1024 threads) and the device's LDS per workgroup.
@@ -138,8 +145,13 @@ int make_plan(const Comm& c, int dev, uint64_t count, DType t, Op op, Plan* p) {
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
     std::vector<uint8_t> orders;
-    if (count / slice_elems >= ((uint64_t)1 << 32)) return EMU_ERR_INVALID_ARGUMENT;   // cell index is 32-bit
-    build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks, &orders);
+    // cell index is 32-bit
+    const uint64_t span = coll == kAllReduce ? count : count * (uint64_t)n;
+    if (span / slice_elems >= ((uint64_t)1 << 32)) return EMU_ERR_INVALID_ARGUMENT;
+    if (coll == kAllReduce)
+      build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks, &orders);
+    else
+      build_ring_coll_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks, &orders);
     p->ntasks = (uint32_t)tasks.size();
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
     if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
@@ -204,6 +216,7 @@ int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t 
   c->chunk_bytes = chunk_bytes;
   if (int e = build_topology(nranks, nnodes, nchannels, pattern, order.data(), &c->topo)) return e;
   if (int e = build_fused_orders(c->topo, c->algo, &c->orders)) return e;
+  if (int e = build_fused_orders(c->topo, Algo::Ring, &c->ring_orders)) return e;
   if (g_comms.size() >= kMaxCachedComms) {
     // Drop every cached communicator except the active one.  Their device
     // tables may still be read by enqueued kernels: wait for the device first.
@@ -224,8 +237,19 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
   return emu_comm_init_graph(nranks, nnodes, algo, nchannels, chunk_bytes, EMU_PATTERN_TREE, nullptr);
 }
 
-int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype, int op,
-                  void* stream) {
+}  // extern "C"
+
+namespace emu {
+namespace {
+
+// Shared by the three collectives: argument checks (before anything is
+// enqueued), plan lookup, launch.  Rank r's send buffer holds send_elems
+// elements and its receive buffer recv_elems; `count` is the all-reduce
+// count or the block size.  In place means recvbufs[r] == sendbufs[r] +
+// inplace_off elements (0 for the all-reduce, r*count for reduce-scatter);
+// for all-gather, sendbufs[r] == recvbufs[r] + r*count.
+int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype,
+                   int op, void* stream) {
   Comm* c = g_active;
   if (!c) return EMU_ERR_NOT_INITIALIZED;
   if (!valid_dtype(dtype) || !valid_op(op) || !sendbufs || !recvbufs) return EMU_ERR_INVALID_ARGUMENT;
@@ -233,31 +257,46 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
   const Op o = static_cast<Op>(op);
   const int n = c->nranks;
   const size_t esz = (size_t)elem_size(t);
-  if (count > ((uint64_t)1 << 40) / esz) return EMU_ERR_INVALID_ARGUMENT;
-  const uint64_t bytes = (uint64_t)count * esz;
+  const uint64_t limit = ((uint64_t)1 << 40) / esz;
+  if (count > limit || (coll != kAllReduce && count > limit / (uint64_t)n)) return EMU_ERR_INVALID_ARGUMENT;
+  // blocks of reduce-scatter / all-gather sit at multiples of count: keep
+  // them 16-byte aligned
+  if (coll != kAllReduce && (count * esz) % kVecBytes) return EMU_ERR_INVALID_ARGUMENT;
+  const uint64_t send_bytes = (coll == kReduceScatter ? (uint64_t)n : 1) * count * esz;
+  const uint64_t recv_bytes = (coll == kAllGather ? (uint64_t)n : 1) * count * esz;
   for (int r = 0; r < n; ++r) {
     if (!sendbufs[r] || !recvbufs[r]) return EMU_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)sendbufs[r] | (uintptr_t)recvbufs[r]) % kVecBytes) return EMU_ERR_INVALID_ARGUMENT;
   }
   if (count == 0) return EMU_SUCCESS;
-  // No two distinct buffers may overlap; a rank's send and receive buffer may
-  // be the same buffer (in place).
-  std::vector<std::pair<uintptr_t, int>> spans;
+  // No two distinct buffers may overlap, except a rank's in-place pair.
+  struct Span { uintptr_t lo, hi; };
+  std::vector<Span> spans;
   for (int r = 0; r < n; ++r) {
-    spans.push_back({(uintptr_t)sendbufs[r], r});
-    if (recvbufs[r] != sendbufs[r]) spans.push_back({(uintptr_t)recvbufs[r], r});
+    const uintptr_t s0 = (uintptr_t)sendbufs[r], r0 = (uintptr_t)recvbufs[r];
+    bool inplace = false;
+    if (coll == kAllReduce) inplace = s0 == r0;
+    else if (coll == kReduceScatter) inplace = r0 == s0 + (uint64_t)r * count * esz;
+    else inplace = s0 == r0 + (uint64_t)r * count * esz;
+    if (inplace) {
+      spans.push_back({std::min(s0, r0), std::max(s0 + send_bytes, r0 + recv_bytes)});
+    } else {
+      spans.push_back({s0, s0 + send_bytes});
+      spans.push_back({r0, r0 + recv_bytes});
+    }
   }
-  std::sort(spans.begin(), spans.end());
+  std::sort(spans.begin(), spans.end(), [](const Span& x, const Span& y) { return x.lo < y.lo; });
   for (size_t i = 1; i < spans.size(); ++i)
-    if (spans[i].first < spans[i - 1].first + bytes) return EMU_ERR_INVALID_ARGUMENT;
+    if (spans[i].lo < spans[i - 1].hi) return EMU_ERR_INVALID_ARGUMENT;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
-  const auto key = std::make_tuple(dev, (uint64_t)count, dtype, c->fused ? 0 : op);
+  const int op_key = (c->fused && coll == kAllReduce) || coll == kAllGather ? 0 : op;
+  const auto key = std::make_tuple(dev, (uint64_t)count, coll == kAllGather ? elem_size(t) : dtype, op_key, (int)coll);
   auto it = c->plans.find(key);
   if (it == c->plans.end()) {
     auto p = std::make_unique<Plan>();
-    if (int e = make_plan(*c, dev, count, t, o, p.get())) return e;
+    if (int e = make_plan(*c, coll, dev, count, t, o, p.get())) return e;
     it = c->plans.emplace(key, std::move(p)).first;
   }
   const Plan& p = *it->second;
@@ -265,15 +304,17 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
   hipError_t err;
   if (c->fused) {
     FusedArgs a{};
-    const FusedOrders& ord = c->orders;
+    const FusedOrders& ord = coll == kAllReduce ? c->orders : c->ring_orders;
     for (int r = 0; r < n; ++r) {
       // kRotate folds pointer j as the j-th rank of the shared order
-      a.send[r] = sendbufs[ord.mode == kRotate ? ord.rotate_perm[r] : r];
+      const bool rotate = ord.mode == kRotate && coll != kAllGather;
+      a.send[r] = sendbufs[rotate ? ord.rotate_perm[r] : r];
       a.recv[r] = recvbufs[r];
     }
+    a.block_bytes = (uint64_t)count * esz;
     a.ntiles = p.ntiles;
     a.nranks = (uint32_t)n;
-    err = launch_fused(t, o, ord.mode, a, static_cast<const Tile*>(p.tiles.ptr),
+    err = launch_fused(coll, t, o, ord.mode, a, static_cast<const Tile*>(p.tiles.ptr),
                        static_cast<const uint32_t*>(p.rows.ptr), p.fused_grid, s);
   } else {
     StepArgs a{};
@@ -282,13 +323,34 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
     a.table = p.table.ptr;
     a.orders = static_cast<const uint8_t*>(p.orders.ptr);
     a.count = count;
+    a.block = count;
     a.ntasks = p.ntasks;
     a.nranks = (uint32_t)n;
     a.group = (uint32_t)p.group;
     a.height = p.height;
-    err = launch_stepwise(c->algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
+    err = launch_stepwise(coll, c->algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
   }
   return err == hipSuccess ? EMU_SUCCESS : EMU_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace emu
+
+extern "C" {
+
+int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype, int op,
+                  void* stream) {
+  return run_collective(kAllReduce, sendbufs, recvbufs, count, dtype, op, stream);
+}
+
+int emu_reduce_scatter(const void* const sendbufs[], void* const recvbufs[], size_t recvcount, int dtype, int op,
+                       void* stream) {
+  return run_collective(kReduceScatter, sendbufs, recvbufs, recvcount, dtype, op, stream);
+}
+
+int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t sendcount, int dtype,
+                   void* stream) {
+  return run_collective(kAllGather, sendbufs, recvbufs, sendcount, dtype, EMU_SUM, stream);
 }
 
 int emu_tree_topology(int channel, int rank, int* up, int down[3]) {

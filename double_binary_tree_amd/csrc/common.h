@@ -27,10 +27,16 @@ inline int elem_size(DType t) {
   return 0;
 }
 
-// A contiguous element range evaluated with one order ("variant"), whose
-// meaning depends on the fused mode (FusedMode): the rank-chunk index k for
-// a rotated fold, or (row << 8) | k for the order rows.  A tile never
-// straddles two variants.
+// Collectives on the ring schedule: the all-reduce, and its two halves run
+// standalone (reduce-scatter: rank r keeps the reduction of block r;
+// all-gather: block k of every output is rank k's input).
+enum Coll : int { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+
+// A contiguous element range evaluated with one order ("variant"): bits
+// 0..7 the start k of the fold (rank-chunk index), bits 8..15 the row of the
+// order table (FusedMode), bits 16..23 the block owner (reduce-scatter: the
+// output rank; all-gather: the source rank).  A tile never straddles two
+// variants.
 struct Tile {
   uint64_t start;     // first element
   uint32_t nelem;     // elements in the tile
@@ -39,9 +45,9 @@ struct Tile {
 static_assert(sizeof(Tile) == 16, "tile layout");
 
 // Fused modes.
-//  kRotate:  input j of variant k is rank (k + j) mod N of the pointer
-//            arrays, which the host passes already permuted into the one
-//            order every channel shares; a plain left fold.
+//  kRotate:  input j is rank (k + j) mod N of the send-pointer array, which
+//            the host passes already permuted into the one order every
+//            channel shares; a plain left fold.
 //  kFold:    input j is rank rows[row][k + j] & 0xFF; a plain left fold.
 //  kProgram: input j is rank rows[row][j] & 0xFF, consumed by the register
 //            program in bits 8..15 of the entry: it goes to register
@@ -55,6 +61,7 @@ constexpr int kRowLen = 2 * kMaxRanks;   // a ring row holds its order twice: k 
 struct FusedArgs {
   const void* send[kMaxRanks];
   void* recv[kMaxRanks];
+  uint64_t block_bytes;       // reduce-scatter / all-gather: bytes per block
   uint32_t ntiles;
   uint32_t nranks;
 };
@@ -95,6 +102,7 @@ struct StepArgs {
   const void* table;          // RingLoopBlock* (ring) or TreeNode* (tree, [nch][nranks])
   const uint8_t* orders;      // ring: [rings][kMaxRanks], position p -> rank
   uint64_t count;             // elements per rank
+  uint64_t block;             // reduce-scatter / all-gather: elements per block
   uint32_t ntasks;
   uint32_t nranks;
   uint32_t group;             // lanes per virtual rank

@@ -1,7 +1,9 @@
-// Fused all-reduce: one pass over HBM.  Each lane owns one 16-byte vector
-// position of the message; it reads that position from every rank's send
-// buffer once, evaluates the element in the schedule's own order, and writes
-// the result to every rank's receive buffer.  2*N*S bytes in total, no LDS.
+// Fused collectives: one pass over HBM.  All-reduce: each lane owns one
+// 16-byte vector position of the message; it reads that position from every
+// rank's send buffer once, evaluates the element in the schedule's own
+// order, and writes the result to every rank's receive buffer (2*N*S bytes
+// in total, no LDS).  Reduce-scatter evaluates the same way but writes only
+// the owner of the block; all-gather copies one input to every output.
 //
 // Orders (see the oracle and the pages):
 //  * ring: rank-chunk k of a channel whose ring visits ranks o_0, o_1, ...
@@ -51,10 +53,10 @@ template <int MODE>
 __device__ __forceinline__ uint32_t order_entry(const FusedArgs& a, const uint32_t* __restrict__ rows,
                                                 uint32_t variant, uint32_t j) {
   if (MODE == kRotate) {
-    const uint32_t r = variant + j;
+    const uint32_t r = (variant & 0xFF) + j;
     return r >= a.nranks ? r - a.nranks : r;
   }
-  return rows[(variant >> 8) * kRowLen + (variant & 0xFF) + j];
+  return rows[((variant >> 8) & 0xFF) * kRowLen + (variant & 0xFF) + j];
 }
 
 // Register stack size: the program mode's stack; the fold modes need none.
@@ -127,21 +129,34 @@ __device__ __forceinline__ void evaluate(const FusedArgs& a, const uint32_t* __r
 }
 
 // The one partial vector at the end of the message: `nbytes` valid bytes,
-// one rank at a time, 16-bit accesses.
-template <typename R, int MODE>
+// one rank at a time, 16-bit accesses.  Reduce-scatter writes only the
+// block owner's output, `shift` bytes lower; all-gather copies from the
+// block owner's input, `shift` bytes lower.
+template <typename R, int MODE, int COLL>
 __device__ __forceinline__ void partial_vector(const FusedArgs& a, const uint32_t* __restrict__ rows,
                                                uint32_t variant, uint64_t boff, int nbytes) {
-  u32x4 acc[1];
-  u32x4 g[stack_regs<MODE>()];
+  const uint32_t owner = variant >> 16;
+  const uint64_t shift = COLL == kAllReduce ? 0 : (uint64_t)owner * a.block_bytes;
+  u32x4 res;
+  if constexpr (COLL == kAllGather) {
+    res = ld_part(a.send[owner], boff - shift, nbytes);
+  } else {
+    u32x4 acc[1];
+    u32x4 g[stack_regs<MODE>()];
 #pragma unroll
-  for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
-  for (uint32_t j = 0; j < a.nranks; ++j) {
-    const uint32_t e = order_entry<MODE>(a, rows, variant, j);
-    const u32x4 x[1] = {ld_part(a.send[e & 0xFF], boff, nbytes)};
-    consume<R, MODE, 1>(e, j, x, acc, g);
+    for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
+    for (uint32_t j = 0; j < a.nranks; ++j) {
+      const uint32_t e = order_entry<MODE>(a, rows, variant, j);
+      const u32x4 x[1] = {ld_part(a.send[e & 0xFF], boff, nbytes)};
+      consume<R, MODE, 1>(e, j, x, acc, g);
+    }
+    res = R::post(MODE == kProgram ? g[0] : acc[0]);
   }
-  const u32x4 res = R::post(MODE == kProgram ? g[0] : acc[0]);
-  for (uint32_t r = 0; r < a.nranks; ++r) st_part(a.recv[r], boff, nbytes, res);
+  if constexpr (COLL == kReduceScatter) {
+    st_part(a.recv[owner], boff - shift, nbytes, res);
+  } else {
+    for (uint32_t r = 0; r < a.nranks; ++r) st_part(a.recv[r], boff, nbytes, res);
+  }
 }
 
 // Write V results to every rank.
@@ -165,13 +180,42 @@ __device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, uin
     for (int v = 0; v < V; ++v) st_vec(a.recv[r], boff + (uint64_t)v * stride, res[v]);
 }
 
+// V whole-vector positions (byte offsets boff + v*stride) of one tile: the
+// all-reduce folds every rank's input there and writes every rank's output;
+// reduce-scatter folds the same way and writes only the block owner's
+// output, one block lower; all-gather copies the block owner's input (one
+// block lower) to every rank's output.
+template <typename R, int MODE, int COLL, int V>
+__device__ __forceinline__ void do_positions(const FusedArgs& a, const uint32_t* __restrict__ rows,
+                                             uint32_t variant, uint64_t boff, uint32_t stride) {
+  const uint32_t owner = variant >> 16;
+  const uint64_t shift = COLL == kAllReduce ? 0 : (uint64_t)owner * a.block_bytes;
+  if constexpr (COLL == kAllGather) {
+    u32x4 x[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[v] = ld_vec(a.send[owner], boff - shift + (uint64_t)v * stride);
+    store_all<V>(a, boff, stride, x);
+  } else {
+    u32x4 res[V];
+    evaluate<R, MODE, V>(a, rows, variant, boff, stride, res);
+    if constexpr (COLL == kReduceScatter) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) st_vec(a.recv[owner], boff - shift + (uint64_t)v * stride, res[v]);
+    } else {
+      store_all<V>(a, boff, stride, res);
+    }
+  }
+}
+
 // A tile holds kFusedThreads * kVpt vectors; lane l owns vectors l, l + 256,
-// ... (each group of 64 lanes touches 1 KiB contiguous per rank).
+// ... (each group of 64 lanes touches 1 KiB contiguous per rank).  Tiles
+// are laid on the input positions (all-reduce, reduce-scatter) or the
+// output positions (all-gather): the side with N accesses per position.
 // The tile table and the order rows come as their own read-only arguments
 // so that the (uniform) loads from them go through the scalar unit.
-template <typename R, int MODE, int ESZ>
-__global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs a, const Tile* __restrict__ tiles,
-                                                                 const uint32_t* __restrict__ rows) {
+template <typename R, int MODE, int ESZ, int COLL>
+__global__ __launch_bounds__(kFusedThreads) void fused_collective(const FusedArgs a, const Tile* __restrict__ tiles,
+                                                                  const uint32_t* __restrict__ rows) {
   constexpr uint32_t unit = kVecBytes / ESZ;
   constexpr uint32_t stride = kFusedThreads * kVecBytes;   // bytes between a lane's vectors
   for (uint32_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
@@ -182,16 +226,10 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs
       if (MODE == kProgram) {
         // The register stack is indexed dynamically; one position at a time
         // keeps it in VGPRs.
-        for (int v = 0; v < kVpt; ++v) {
-          u32x4 res[1];
-          evaluate<R, MODE, 1>(a, rows, tile.variant, base + lane_off + (uint64_t)v * stride, 0, res);
-          store_all<1>(a, base + lane_off + (uint64_t)v * stride, 0, res);
-        }
+        for (int v = 0; v < kVpt; ++v)
+          do_positions<R, MODE, COLL, 1>(a, rows, tile.variant, base + lane_off + (uint64_t)v * stride, 0);
       } else {
-        constexpr int V = MODE == kProgram ? 1 : kVpt;
-        u32x4 res[V];
-        evaluate<R, MODE, V>(a, rows, tile.variant, base + lane_off, stride, res);
-        store_all<V>(a, base + lane_off, stride, res);
+        do_positions<R, MODE, COLL, kVpt>(a, rows, tile.variant, base + lane_off, stride);
       }
       continue;
     }
@@ -204,50 +242,59 @@ __global__ __launch_bounds__(kFusedThreads) void fused_allreduce(const FusedArgs
       const uint64_t pos = cell + (uint64_t)(threadIdx.x + v * kFusedThreads) * unit;
       if (pos < tile.start || pos >= end) continue;
       const uint64_t boff = pos * ESZ;
-      if (end - pos >= unit) {
-        u32x4 res[1];
-        evaluate<R, MODE, 1>(a, rows, tile.variant, boff, 0, res);
-        store_all<1>(a, boff, 0, res);
-      } else {
-        partial_vector<R, MODE>(a, rows, tile.variant, boff, (int)((end - pos) * ESZ));
-      }
+      if (end - pos >= unit)
+        do_positions<R, MODE, COLL, 1>(a, rows, tile.variant, boff, 0);
+      else
+        partial_vector<R, MODE, COLL>(a, rows, tile.variant, boff, (int)((end - pos) * ESZ));
     }
   }
 }
 
-template <DType T, Op O, int MODE>
+template <DType T, Op O, int MODE, int COLL>
 static hipError_t launch_one(const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
                              hipStream_t stream) {
-  hipLaunchKernelGGL((fused_allreduce<Red<T, O>, MODE, Unit<T>::esz>), dim3(grid), dim3(kFusedThreads),
+  hipLaunchKernelGGL((fused_collective<Red<T, O>, MODE, Unit<T>::esz, COLL>), dim3(grid), dim3(kFusedThreads),
                      0, stream, a, tiles, rows);
   return hipGetLastError();
 }
 
 template <DType T, Op O>
-static hipError_t launch_mode(int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
-                              hipStream_t stream) {
+static hipError_t launch_mode(Coll coll, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows,
+                              int grid, hipStream_t stream) {
+  if (coll == kReduceScatter)   // ring orders only: no register programs
+    return mode == kRotate ? launch_one<T, O, kRotate, kReduceScatter>(a, tiles, rows, grid, stream)
+                           : launch_one<T, O, kFold, kReduceScatter>(a, tiles, rows, grid, stream);
   switch (mode) {
-    case kRotate: return launch_one<T, O, kRotate>(a, tiles, rows, grid, stream);
-    case kFold: return launch_one<T, O, kFold>(a, tiles, rows, grid, stream);
-    default: return launch_one<T, O, kProgram>(a, tiles, rows, grid, stream);
+    case kRotate: return launch_one<T, O, kRotate, kAllReduce>(a, tiles, rows, grid, stream);
+    case kFold: return launch_one<T, O, kFold, kAllReduce>(a, tiles, rows, grid, stream);
+    default: return launch_one<T, O, kProgram, kAllReduce>(a, tiles, rows, grid, stream);
   }
 }
 
 template <DType T>
-static hipError_t launch_op(Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
-                            hipStream_t stream) {
-  return op == Op::Sum ? launch_mode<T, Op::Sum>(mode, a, tiles, rows, grid, stream)
-                       : launch_mode<T, Op::Max>(mode, a, tiles, rows, grid, stream);
+static hipError_t launch_op(Coll coll, Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows,
+                            int grid, hipStream_t stream) {
+  return op == Op::Sum ? launch_mode<T, Op::Sum>(coll, mode, a, tiles, rows, grid, stream)
+                       : launch_mode<T, Op::Max>(coll, mode, a, tiles, rows, grid, stream);
 }
 
-hipError_t launch_fused(DType t, Op op, int mode, const FusedArgs& a, const Tile* tiles, const uint32_t* rows,
-                        int grid, hipStream_t stream) {
+hipError_t launch_fused(Coll coll, DType t, Op op, int mode, const FusedArgs& a, const Tile* tiles,
+                        const uint32_t* rows, int grid, hipStream_t stream) {
+  if (coll == kAllGather) {
+    // a copy: only the element size matters
+    switch (elem_size(t)) {
+      case 2: return launch_one<DType::F16, Op::Sum, kRotate, kAllGather>(a, tiles, rows, grid, stream);
+      case 4: return launch_one<DType::I32, Op::Sum, kRotate, kAllGather>(a, tiles, rows, grid, stream);
+      case 8: return launch_one<DType::I64, Op::Sum, kRotate, kAllGather>(a, tiles, rows, grid, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (t) {
-    case DType::I32: return launch_op<DType::I32>(op, mode, a, tiles, rows, grid, stream);
-    case DType::I64: return launch_op<DType::I64>(op, mode, a, tiles, rows, grid, stream);
-    case DType::F32: return launch_op<DType::F32>(op, mode, a, tiles, rows, grid, stream);
-    case DType::F16: return launch_op<DType::F16>(op, mode, a, tiles, rows, grid, stream);
-    case DType::BF16: return launch_op<DType::BF16>(op, mode, a, tiles, rows, grid, stream);
+    case DType::I32: return launch_op<DType::I32>(coll, op, mode, a, tiles, rows, grid, stream);
+    case DType::I64: return launch_op<DType::I64>(coll, op, mode, a, tiles, rows, grid, stream);
+    case DType::F32: return launch_op<DType::F32>(coll, op, mode, a, tiles, rows, grid, stream);
+    case DType::F16: return launch_op<DType::F16>(coll, op, mode, a, tiles, rows, grid, stream);
+    case DType::BF16: return launch_op<DType::BF16>(coll, op, mode, a, tiles, rows, grid, stream);
   }
   return hipErrorInvalidValue;
 }

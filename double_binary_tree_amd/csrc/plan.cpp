@@ -58,19 +58,50 @@ std::vector<std::vector<Range>> ring_loops(const Range& ch, int nranks, uint64_t
   return loops;
 }
 
-void build_fused_tiles(const Topology& topo, Algo algo, const FusedOrders& orders, uint64_t count,
-                       uint64_t unit, uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out) {
-  // Segments (start, length, variant) in element order, adjacent segments of
-  // equal variant merged.
+namespace {
+
+// Segments (start, length, variant) in element order, adjacent segments of
+// equal variant merged.
+struct Segments {
   struct Seg { uint64_t start, len; uint32_t variant; };
   std::vector<Seg> segs;
-  auto push = [&](uint64_t s, uint64_t n, uint32_t v) {
+  void push(uint64_t s, uint64_t n, uint32_t v) {
     if (n == 0) return;
     if (!segs.empty() && segs.back().variant == v && segs.back().start + segs.back().len == s)
       segs.back().len += n;
     else
       segs.push_back({s, n, v});
-  };
+  }
+  // Cut at global multiples of the tile size, so that full tiles start on a
+  // tile-size (>= 4 KiB) boundary of every rank buffer and each wave's
+  // accesses cover whole cache lines; only the pieces next to a segment
+  // boundary are short.
+  void cut(uint64_t tile_elems, std::vector<Tile>* out) const {
+    out->clear();
+    for (const Seg& s : segs) {
+      uint64_t pos = s.start;
+      const uint64_t end = s.start + s.len;
+      while (pos < end) {
+        const uint64_t next = std::min(end, (pos / tile_elems + 1) * tile_elems);
+        out->push_back({pos, (uint32_t)(next - pos), s.variant});
+        pos = next;
+      }
+    }
+  }
+};
+
+int position_of(const ChannelTopology& ch, int rank) {
+  for (size_t p = 0; p < ch.order.size(); ++p)
+    if (ch.order[p] == rank) return (int)p;
+  return 0;
+}
+
+}  // namespace
+
+void build_fused_tiles(const Topology& topo, Algo algo, const FusedOrders& orders, uint64_t count,
+                       uint64_t unit, uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out) {
+  Segments sg;
+  auto push = [&](uint64_t s, uint64_t n, uint32_t v) { sg.push(s, n, v); };
   const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
   for (int c = 0; c < topo.nchannels; ++c) {
     if (algo == Algo::Ring) {
@@ -80,18 +111,49 @@ void build_fused_tiles(const Topology& topo, Algo algo, const FusedOrders& order
       push(chans[c].offset, chans[c].count, orders.base[c]);
     }
   }
-  // Cut at global multiples of the tile size, so that full tiles start on a
-  // tile-size (>= 4 KiB) boundary of every rank buffer and each wave's
-  // accesses cover whole cache lines; only the pieces next to a segment
-  // boundary are short.
-  out->clear();
-  for (const Seg& s : segs) {
-    uint64_t pos = s.start;
-    const uint64_t end = s.start + s.len;
-    while (pos < end) {
-      const uint64_t next = std::min(end, (pos / tile_elems + 1) * tile_elems);
-      out->push_back({pos, (uint32_t)(next - pos), s.variant});
-      pos = next;
+  sg.cut(tile_elems, out);
+}
+
+void build_fused_coll_tiles(const Topology& topo, Coll coll, const FusedOrders& ring_orders, uint64_t block,
+                            uint64_t unit, uint64_t tile_elems, std::vector<Tile>* out) {
+  const int n = topo.nranks;
+  Segments sg;
+  if (coll == kAllGather) {
+    for (int k = 0; k < n; ++k) sg.push((uint64_t)k * block, block, (uint32_t)k << 16);
+  } else {
+    const std::vector<Range> chans = channel_ranges(block, unit, topo.nchannels);
+    for (int r = 0; r < n; ++r)
+      for (int c = 0; c < topo.nchannels; ++c) {
+        const uint32_t k = (uint32_t)((position_of(topo.channels[c], r) + 1) % n);
+        sg.push((uint64_t)r * block + chans[c].offset, chans[c].count, (uint32_t)r << 16 | (ring_orders.base[c] + k));
+      }
+  }
+  sg.cut(tile_elems, out);
+}
+
+void build_ring_coll_tasks(const Topology& topo, uint64_t block, uint64_t unit, uint64_t chunk_count,
+                           uint64_t slice_elems, std::vector<RingLoopBlock>* loops, std::vector<RingTask>* tasks,
+                           std::vector<uint8_t>* orders) {
+  const int n = topo.nranks;
+  loops->clear();
+  tasks->clear();
+  orders->assign((size_t)topo.nrings * kMaxRanks, 0);
+  for (const ChannelTopology& c : topo.channels)
+    for (int p = 0; p < n; ++p) (*orders)[(size_t)c.ring_id * kMaxRanks + p] = (uint8_t)c.order[p];
+  uint32_t loop_id = 0;
+  const std::vector<Range> chans = channel_ranges(block, unit, topo.nchannels);
+  for (int c = 0; c < topo.nchannels; ++c) {
+    const ChannelTopology& ch = topo.channels[c];
+    for (const Range& piece : tree_chunks(chans[c], chunk_count)) {
+      uint64_t nslices = 0;
+      for (int k = 0; k < n; ++k) {
+        const uint64_t d = (uint64_t)ch.order[(k + n - 1) % n];   // data block of step block k
+        const uint64_t off = d * block + piece.offset;
+        loops->push_back({off, (uint32_t)piece.count, (uint32_t)(off / slice_elems)});
+        nslices = std::max(nslices, ceil_div(off + piece.count, slice_elems) - off / slice_elems);
+      }
+      for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q, (uint32_t)ch.ring_id, 0});
+      ++loop_id;
     }
   }
 }

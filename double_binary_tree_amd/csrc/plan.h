@@ -48,6 +48,21 @@ int build_fused_orders(const Topology& topo, Algo algo, FusedOrders* out);
 void build_fused_tiles(const Topology& topo, Algo algo, const FusedOrders& orders, uint64_t count,
                        uint64_t unit, uint64_t chunk_count, uint64_t tile_elems, std::vector<Tile>* out);
 
+// Reduce-scatter / all-gather, fused: tiles over the input positions
+// (reduce-scatter: block r of every input, folded in channel c's ring order
+// from the position after r's) or the output positions (all-gather: block k
+// of every output, copied from rank k).  `block` elements per block.
+void build_fused_coll_tiles(const Topology& topo, Coll coll, const FusedOrders& ring_orders, uint64_t block,
+                            uint64_t unit, uint64_t tile_elems, std::vector<Tile>* out);
+
+// Reduce-scatter / all-gather, stepwise: per channel range of a block and
+// chunk, one loop of nranks step-schedule blocks; step block k is data block
+// order[k-1] (so that position p finishes, or starts from, its own rank's
+// block).  Loop table, tasks and ring orders as for build_ring_tasks.
+void build_ring_coll_tasks(const Topology& topo, uint64_t block, uint64_t unit, uint64_t chunk_count,
+                           uint64_t slice_elems, std::vector<RingLoopBlock>* loops, std::vector<RingTask>* tasks,
+                           std::vector<uint8_t>* orders);
+
 // Stepwise ring: loop table (nranks blocks per loop), tasks (loop, slice,
 // ring order) and the ring order table ([nrings][kMaxRanks]).
 void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,

@@ -54,7 +54,12 @@ __device__ __forceinline__ void step_barrier() {
 #define EMU_TREE_PREFETCH 1
 #endif
 
-template <typename R, int ESZ>
+// COLL selects the collective: the all-reduce runs both halves; the
+// standalone reduce-scatter stops after its N-1 steps and writes the
+// finished block (the position's own block) to its rank's output, one
+// block lower; the standalone all-gather starts from each position's own
+// input (one block lower) and runs only the N-1 forwarding steps.
+template <typename R, int ESZ, int COLL>
 __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_RING_VPT;
@@ -89,6 +94,10 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
     const RingTask task = tasks[t];
     const RingLoopBlock* blk = desc + set * n;
     const uint32_t me = active ? order[set * kMaxRanks + r] : 0;   // the rank at position r
+    // byte distance between a block's place and the rank's own buffer
+    const uint64_t my_shift = COLL == kAllReduce ? 0 : (uint64_t)me * a.block * ESZ;
+    const uint64_t load_shift = COLL == kAllGather ? my_shift : 0;
+    const uint64_t store_shift = COLL == kReduceScatter ? my_shift : 0;
     if (n > 1) stage_desc(t + gridDim.x, set ^ 1);   // visible after this task's barriers
     // Slice q of block b is the q-th slice-size cell of the global element
     // grid that the block overlaps; lane p's vector v sits at a fixed place in
@@ -108,14 +117,14 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int nb = nbytes_of(b, v);
-        x[v] = nb ? ld_any(a.send[me], boff_of(b, v), nb) : u32x4{0, 0, 0, 0};
+        x[v] = nb ? ld_any(a.send[me], boff_of(b, v) - load_shift, nb) : u32x4{0, 0, 0, 0};
       }
     };
     auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int nb = nbytes_of(b, v);
-        if (nb) st_any(a.recv[me], boff_of(b, v), nb, R::post(x[v]));
+        if (nb) st_any(a.recv[me], boff_of(b, v) - store_shift, nb, R::post(x[v]));
       }
     };
 
@@ -131,6 +140,18 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
       step_barrier();
       continue;
     }
+    if constexpr (COLL == kAllGather) {
+      // the position's own input is the finished block (r+1) mod N: write it
+      // to its own output and into the slot the forwarding steps read first
+      if (active) {
+        u32x4 own[V];
+        load_block((r + 1) % n, own);
+        store_block((r + 1) % n, own);
+#pragma unroll
+        for (int v = 0; v < V; ++v) slot((n - 1) & 1, r, v) = R::pre(own[v]);
+      }
+      step_barrier();
+    } else {
     // step 0: send own block r; the blocks of steps 1..PF are loaded ahead
     // (queue q[0] is the next step's block).
     u32x4 own[V], q[kPrefetch][V];
@@ -165,6 +186,8 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
       }
       step_barrier();
     }
+    }
+    if (COLL == kReduceScatter) continue;
     // all-gather steps 1..N-1
     for (uint32_t j = 1; j < n; ++j) {
       const uint32_t b = (r + 1 + n - j) % n;
@@ -307,10 +330,10 @@ static hipError_t allow_lds(K kernel, size_t lds) {
                              (int)lds);
 }
 
-template <DType T, Op O>
+template <DType T, Op O, int COLL>
 static hipError_t launch_ring_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz>, lds)) return e;
-  hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz>), dim3(grid), dim3(block), lds, s, a);
+  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz, COLL>, lds)) return e;
+  hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz, COLL>), dim3(grid), dim3(block), lds, s, a);
   return hipGetLastError();
 }
 template <DType T, Op O>
@@ -321,51 +344,71 @@ static hipError_t launch_tree_t(const StepArgs& a, int grid, int block, size_t l
 }
 
 template <DType T>
-static hipError_t launch_step_t(bool ring, Op op, const StepArgs& a, int grid, int block, size_t lds,
+static hipError_t launch_step_t(Coll coll, bool ring, Op op, const StepArgs& a, int grid, int block, size_t lds,
                                 hipStream_t s) {
+  if (coll == kReduceScatter)
+    return op == Op::Sum ? launch_ring_t<T, Op::Sum, kReduceScatter>(a, grid, block, lds, s)
+                         : launch_ring_t<T, Op::Max, kReduceScatter>(a, grid, block, lds, s);
   if (ring)
-    return op == Op::Sum ? launch_ring_t<T, Op::Sum>(a, grid, block, lds, s)
-                         : launch_ring_t<T, Op::Max>(a, grid, block, lds, s);
+    return op == Op::Sum ? launch_ring_t<T, Op::Sum, kAllReduce>(a, grid, block, lds, s)
+                         : launch_ring_t<T, Op::Max, kAllReduce>(a, grid, block, lds, s);
   return op == Op::Sum ? launch_tree_t<T, Op::Sum>(a, grid, block, lds, s)
                        : launch_tree_t<T, Op::Max>(a, grid, block, lds, s);
 }
 
-hipError_t launch_stepwise(bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
+hipError_t launch_stepwise(Coll coll, bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
                            size_t lds, hipStream_t s) {
+  if (coll == kAllGather) {
+    // a copy: only the element size matters
+    switch (elem_size(t)) {
+      case 2: return launch_ring_t<DType::F16, Op::Sum, kAllGather>(a, grid, block, lds, s);
+      case 4: return launch_ring_t<DType::I32, Op::Sum, kAllGather>(a, grid, block, lds, s);
+      case 8: return launch_ring_t<DType::I64, Op::Sum, kAllGather>(a, grid, block, lds, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (t) {
-    case DType::I32: return launch_step_t<DType::I32>(ring, op, a, grid, block, lds, s);
-    case DType::I64: return launch_step_t<DType::I64>(ring, op, a, grid, block, lds, s);
-    case DType::F32: return launch_step_t<DType::F32>(ring, op, a, grid, block, lds, s);
-    case DType::F16: return launch_step_t<DType::F16>(ring, op, a, grid, block, lds, s);
-    case DType::BF16: return launch_step_t<DType::BF16>(ring, op, a, grid, block, lds, s);
+    case DType::I32: return launch_step_t<DType::I32>(coll, ring, op, a, grid, block, lds, s);
+    case DType::I64: return launch_step_t<DType::I64>(coll, ring, op, a, grid, block, lds, s);
+    case DType::F32: return launch_step_t<DType::F32>(coll, ring, op, a, grid, block, lds, s);
+    case DType::F16: return launch_step_t<DType::F16>(coll, ring, op, a, grid, block, lds, s);
+    case DType::BF16: return launch_step_t<DType::BF16>(coll, ring, op, a, grid, block, lds, s);
   }
   return hipErrorInvalidValue;
 }
 
 int stepwise_vectors_per_lane(bool ring) { return ring ? EMU_RING_VPT : EMU_TREE_VPT; }
 
-// Resident workgroups per CU for the stepwise kernels at this block/LDS size.
-int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds) {
+template <typename K>
+static int occupancy_of(K kernel, int block, size_t lds) {
   int blocks = 0;
-  hipError_t e = hipErrorInvalidValue;
-#define EMU_OCC(T_)                                                                                 \
-  if (t == T_) {                                                                                    \
-    if (ring)                                                                                       \
-      e = op == Op::Sum                                                                             \
-              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_ring<Red<T_, Op::Sum>, Unit<T_>::esz>, block, lds) \
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_ring<Red<T_, Op::Max>, Unit<T_>::esz>, block, lds); \
-    else                                                                                            \
-      e = op == Op::Sum                                                                             \
-              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_tree<Red<T_, Op::Sum>, Unit<T_>::esz>, block, lds) \
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_tree<Red<T_, Op::Max>, Unit<T_>::esz>, block, lds); \
-  }
-  EMU_OCC(DType::I32)
-  EMU_OCC(DType::I64)
-  EMU_OCC(DType::F32)
-  EMU_OCC(DType::F16)
-  EMU_OCC(DType::BF16)
-#undef EMU_OCC
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, block, lds);
   return e == hipSuccess && blocks > 0 ? blocks : 1;
+}
+
+template <DType T, Op O>
+static int occupancy_t(bool ring, int block, size_t lds) {
+  return ring ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce>, block, lds)
+              : occupancy_of(step_tree<Red<T, O>, Unit<T>::esz>, block, lds);
+}
+
+// Resident workgroups per CU for the stepwise kernels at this block/LDS size
+// (the ring all-reduce kernel stands for its reduce-scatter and all-gather
+// forms, which use no more registers).
+int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds) {
+  switch (t) {
+    case DType::I32: return op == Op::Sum ? occupancy_t<DType::I32, Op::Sum>(ring, block, lds)
+                                          : occupancy_t<DType::I32, Op::Max>(ring, block, lds);
+    case DType::I64: return op == Op::Sum ? occupancy_t<DType::I64, Op::Sum>(ring, block, lds)
+                                          : occupancy_t<DType::I64, Op::Max>(ring, block, lds);
+    case DType::F32: return op == Op::Sum ? occupancy_t<DType::F32, Op::Sum>(ring, block, lds)
+                                          : occupancy_t<DType::F32, Op::Max>(ring, block, lds);
+    case DType::F16: return op == Op::Sum ? occupancy_t<DType::F16, Op::Sum>(ring, block, lds)
+                                          : occupancy_t<DType::F16, Op::Max>(ring, block, lds);
+    case DType::BF16: return op == Op::Sum ? occupancy_t<DType::BF16, Op::Sum>(ring, block, lds)
+                                           : occupancy_t<DType::BF16, Op::Max>(ring, block, lds);
+  }
+  return 1;
 }
 
 }  // namespace emu

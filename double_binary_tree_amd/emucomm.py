@@ -50,6 +50,12 @@ def lib() -> ctypes.CDLL:
         L.emu_allreduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                     ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.emu_allreduce.restype = ctypes.c_int
+        L.emu_reduce_scatter.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_reduce_scatter.restype = ctypes.c_int
+        L.emu_all_gather.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                     ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+        L.emu_all_gather.restype = ctypes.c_int
         L.emu_tree_topology.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_int)]
         L.emu_tree_topology.restype = ctypes.c_int
@@ -120,6 +126,27 @@ def allreduce(sendptrs, recvptrs, count: int, dtype: str, op: str, stream: int =
     _check(allreduce_raw(sendptrs, recvptrs, count, DTYPE[dtype], OP[op], stream), "emu_allreduce")
 
 
+def _ptrs(ptrs):
+    return (ctypes.c_void_p * max(len(ptrs), 1))(*[ctypes.c_void_p(int(p)) for p in ptrs])
+
+
+def reduce_scatter_raw(sendptrs, recvptrs, recvcount: int, dtype: int, op: int, stream: int = 0) -> int:
+    return lib().emu_reduce_scatter(_ptrs(sendptrs), _ptrs(recvptrs), recvcount, dtype, op,
+                                    ctypes.c_void_p(int(stream)))
+
+
+def reduce_scatter(sendptrs, recvptrs, recvcount: int, dtype: str, op: str, stream: int = 0) -> None:
+    _check(reduce_scatter_raw(sendptrs, recvptrs, recvcount, DTYPE[dtype], OP[op], stream), "emu_reduce_scatter")
+
+
+def all_gather_raw(sendptrs, recvptrs, sendcount: int, dtype: int, stream: int = 0) -> int:
+    return lib().emu_all_gather(_ptrs(sendptrs), _ptrs(recvptrs), sendcount, dtype, ctypes.c_void_p(int(stream)))
+
+
+def all_gather(sendptrs, recvptrs, sendcount: int, dtype: str, stream: int = 0) -> None:
+    _check(all_gather_raw(sendptrs, recvptrs, sendcount, DTYPE[dtype], stream), "emu_all_gather")
+
+
 def tree_topology(channel: int, rank: int) -> tuple[int, list[int]]:
     up = ctypes.c_int(0)
     down = (ctypes.c_int * 3)()
@@ -158,3 +185,39 @@ def allreduce_tensors(sends, recvs, op: str = "sum", stream=None) -> None:
             raise ValueError("tensors must be contiguous CUDA tensors of one shape and dtype")
     s = torch.cuda.current_stream() if stream is None else stream
     allreduce([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], count, dt, op, s.cuda_stream)
+
+
+def _check_tensors(ts, numel, dt):
+    import torch
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.numel() != numel or torch_dtype_name(t) != dt:
+            raise ValueError("tensors must be contiguous CUDA tensors of the collective's size and one dtype")
+    del torch
+
+
+def reduce_scatter_tensors(sends, recvs, op: str = "sum", stream=None) -> None:
+    """Reduce-scatter per-rank CUDA tensors: ``sends[r]`` holds nranks blocks
+    of ``recvs[r].numel()`` elements; ``recvs[r]`` gets the reduced block r."""
+    import torch
+    if len(sends) != len(recvs) or not sends:
+        raise ValueError("need one send and one receive tensor per rank")
+    dt = torch_dtype_name(sends[0])
+    rc = recvs[0].numel()
+    _check_tensors(sends, rc * len(sends), dt)
+    _check_tensors(recvs, rc, dt)
+    s = torch.cuda.current_stream() if stream is None else stream
+    reduce_scatter([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], rc, dt, op, s.cuda_stream)
+
+
+def all_gather_tensors(sends, recvs, stream=None) -> None:
+    """All-gather per-rank CUDA tensors: block k of every ``recvs[r]`` gets
+    ``sends[k]``."""
+    import torch
+    if len(sends) != len(recvs) or not sends:
+        raise ValueError("need one send and one receive tensor per rank")
+    dt = torch_dtype_name(sends[0])
+    sc = sends[0].numel()
+    _check_tensors(sends, sc, dt)
+    _check_tensors(recvs, sc * len(sends), dt)
+    s = torch.cuda.current_stream() if stream is None else stream
+    all_gather([t.data_ptr() for t in sends], [t.data_ptr() for t in recvs], sc, dt, s.cuda_stream)

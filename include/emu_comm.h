@@ -158,6 +158,45 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
                   int dtype, int op, void* stream);
 
 /*
+ * emu_reduce_scatter - enqueue one reduce-scatter on `stream`: the first
+ * half of the ring all-reduce run on its own (page "all-reduce 每张卡要发多少
+ * 数据? ring 和 tree 有什么区别?", section "先弄清楚:每个概念是什么" and
+ * Figure 1; page "NCCL代码分析", section "通讯时如何选择Channel": a ring-only
+ * collective).  Uses the active communicator's channels, chunk size, rank
+ * orders and mode; it runs on the ring whatever the communicator's `algo`.
+ *   sendbufs[r]  nranks blocks of `recvcount` elements
+ *   recvbufs[r]  `recvcount` elements: the reduction of block r over all
+ *                ranks, folded in each channel's ring order starting at the
+ *                position after rank r's and ending at rank r (the ring's
+ *                reduce-scatter steps, arranged so that every rank finishes
+ *                its own block), each op rounded as for emu_allreduce.
+ *   recvcount    elements per block; recvcount * element size must be a
+ *                multiple of 16 (every block 16-byte aligned); 0 is a no-op.
+ *   dtype, op    as for emu_allreduce.
+ * In place: recvbufs[r] == sendbufs[r] + r * recvcount elements.  Any other
+ * overlap is invalid.  Pointers non-NULL and 16-byte aligned; nranks *
+ * recvcount * element size at most 2^40 bytes.  Ownership, asynchrony and
+ * errors as for emu_allreduce.
+ */
+int emu_reduce_scatter(const void* const sendbufs[], void* const recvbufs[], size_t recvcount,
+                       int dtype, int op, void* stream);
+
+/*
+ * emu_all_gather - enqueue one all-gather on `stream`: the second half of
+ * the ring all-reduce run on its own (same passages; ring only).  Every
+ * rank's output gets rank k's `sendcount` input elements in block k, bit
+ * for bit.
+ *   sendbufs[r]  `sendcount` elements
+ *   recvbufs[r]  nranks blocks of `sendcount` elements
+ *   sendcount    sendcount * element size must be a multiple of 16; 0 is a
+ *                no-op.
+ * In place: sendbufs[r] == recvbufs[r] + r * sendcount elements.  Other
+ * rules as for emu_reduce_scatter.
+ */
+int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t sendcount, int dtype,
+                   void* stream);
+
+/*
  * emu_tree_topology - the tree record of `rank` in `channel`: its parent
  * (*up, -1 at the root) and its three child slots (down[0..2], -1 when
  * empty), in the order they were filled (intra-node child first, then the

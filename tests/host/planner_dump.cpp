@@ -75,6 +75,32 @@ int main(int argc, char** argv) {
     build_fused_tiles(topo, a, orders, count, unit, chunk, 256 * unit, &tiles);
     print_orders(algo == 0 ? "fused_ring" : "fused_tree", orders, tiles);
   }
+  // reduce-scatter / all-gather with a block of count rounded down to whole units
+  {
+    const uint64_t block = count / unit * unit;
+    FusedOrders ring_orders;
+    build_fused_orders(topo, Algo::Ring, &ring_orders);
+    for (int coll = kReduceScatter; coll <= kAllGather; ++coll) {
+      std::vector<Tile> tiles;
+      build_fused_coll_tiles(topo, (Coll)coll, ring_orders, block, unit, 256 * unit, &tiles);
+      print_orders(coll == kReduceScatter ? "fused_rs" : "fused_ag", ring_orders, tiles);
+    }
+    std::vector<RingLoopBlock> loops;
+    std::vector<RingTask> tasks;
+    std::vector<uint8_t> orders;
+    const uint64_t slice = 64 * unit;
+    build_ring_coll_tasks(topo, block, unit, chunk, slice, &loops, &tasks, &orders);
+    std::printf("\"coll_block\": %llu, \"coll_blocks\": [", (unsigned long long)block);
+    for (size_t i = 0; i < loops.size(); ++i)
+      std::printf("%s[%llu,%u,%u]", i ? "," : "", (unsigned long long)loops[i].offset, loops[i].nelem,
+                  loops[i].first_cell);
+    std::printf("], \"coll_tasks\": [");
+    for (size_t i = 0; i < tasks.size(); ++i)
+      std::printf("%s[%u,%u,%u]", i ? "," : "", tasks[i].loop, tasks[i].slice, tasks[i].ring);
+    std::printf("], \"coll_orders\": [");
+    for (size_t i = 0; i < orders.size(); ++i) std::printf("%s%u", i ? "," : "", orders[i]);
+    std::printf("],");
+  }
   // stepwise ring loop table and tasks, slice of 64 lanes x 1 vector
   {
     std::vector<RingLoopBlock> loops;

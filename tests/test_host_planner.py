@@ -263,6 +263,66 @@ def test_tree_programs_equal_the_oracle_fold(dump, n, m, nch, chunk, esz, count,
             assert prog["pure"] == 1   # a chain is a plain fold
 
 
+@pytest.mark.parametrize("n,m,nch,chunk,esz,count,pattern,seed", ALL)
+def test_collective_tiles_follow_the_oracle(dump, n, m, nch, chunk, esz, count, pattern, seed):
+    # Reduce-scatter: tile elements of block r fold channel c's ring order
+    # from the position after r's; all-gather: tile elements of block k come
+    # from rank k.  Tiles cover the N blocks exactly.
+    d = _dump(dump, n, m, nch, chunk, esz, count, pattern, seed)
+    unit = 16 // esz
+    topo = _topo(n, m, nch, pattern, seed)
+    block = d["coll_block"]
+    assert block == count // unit * unit
+    chan = np.full(block, -1, dtype=np.int64)
+    for c, (off, ln) in enumerate(P.channel_ranges(block, unit, nch)):
+        chan[off:off + ln] = c
+    for key in ("fused_rs", "fused_ag"):
+        fo = d[key]
+        _covers([(s_, ln) for s_, ln, _ in fo["tiles"]], n * block)
+        for s_, ln, v in fo["tiles"]:
+            owner = v >> 16
+            assert s_ // block == owner and (s_ + ln - 1) // block == owner
+            if key == "fused_ag":
+                continue
+            seq, words = _decode(fo, v & 0xFFFF, n)
+            assert words is None
+            for c in set(chan[s_ - owner * block: s_ - owner * block + ln].tolist()):
+                order = topo.channels[c].order
+                p = order.index(owner)
+                assert seq == [order[(p + 1 + j) % n] for j in range(n)], (owner, c)
+
+
+@pytest.mark.parametrize("n,m,nch,chunk,esz,count,pattern,seed", ALL)
+def test_stepwise_collective_tasks(dump, n, m, nch, chunk, esz, count, pattern, seed):
+    # Per channel range of a block and chunk piece: one loop whose step
+    # block k is data block order[k-1] at that piece; tasks cover each block.
+    d = _dump(dump, n, m, nch, chunk, esz, count, pattern, seed)
+    unit = 16 // esz
+    topo = _topo(n, m, nch, pattern, seed)
+    block, slice_ = d["coll_block"], d["ring_slice"]
+    want, loop_chan = [], []
+    for c, (off, ln) in enumerate(P.channel_ranges(block, unit, nch)):
+        order = topo.channels[c].order
+        for o, piece in P.tree_chunks(off, ln, chunk // esz):
+            want.extend((order[(k - 1) % n] * block + o, piece) for k in range(n))
+            loop_chan.append(c)
+    blocks = d["coll_blocks"]
+    assert [(o, b) for o, b, _ in blocks] == want
+    assert all(c == o // slice_ for o, _, c in blocks)
+    orders = d["coll_orders"]
+    per_loop = {}
+    for lp, q, ring in d["coll_tasks"]:
+        per_loop.setdefault(lp, []).append(q)
+        assert orders[ring * 64: ring * 64 + n] == topo.channels[loop_chan[lp]].order
+    assert sorted(per_loop) == list(range(len(loop_chan)))
+    for lp, qs in per_loop.items():
+        assert qs == list(range(len(qs)))
+        for k in range(n):
+            o, b, c = blocks[lp * n + k]
+            covered = sum(max(0, min((c + q + 1) * slice_, o + b) - max((c + q) * slice_, o)) for q in qs)
+            assert covered == b
+
+
 def test_rejected_graphs(dump):
     assert dump(4, 4, 2, 64, 4, 10, 1, None) == {"error": 1}            # split needs two ranks per node
     assert dump(4, 2, 1, 64, 4, 10, 0, [[0, 2, 1, 3]]) == {"error": 1}  # rank 2 is not on node 0

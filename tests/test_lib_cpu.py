@@ -184,3 +184,31 @@ def test_allreduce_argument_errors_without_gpu():
 def test_strerror_total():
     for code in range(-1, 7):
         assert isinstance(E.strerror(code), str) and E.strerror(code)
+
+
+def test_collective_argument_errors_without_gpu():
+    # Reduce-scatter / all-gather checks run before any device call.
+    E.comm_init(2, 1, "tree", 2, 1 << 19, mode="fused")
+    base = 1 << 32
+    rc = 1024                      # f32: 4 KiB blocks
+    send = [base, base + 16384]    # 2 blocks each
+    recv = [base + 32768, base + 36864]
+    rs, ag = E.reduce_scatter_raw, E.all_gather_raw
+    assert rs(send, recv, 0, 2, 0) == E.SUCCESS
+    assert ag(recv, send, 0, 2) == E.SUCCESS
+    assert rs(send, recv, 3, 2, 0) == E.ERR_INVALID_ARGUMENT        # 12-byte blocks are not 16-byte aligned
+    assert ag(recv, send, 5, 3) == E.ERR_INVALID_ARGUMENT           # 10-byte blocks
+    assert rs(send, recv, rc, 9, 0) == E.ERR_INVALID_ARGUMENT       # dtype
+    assert rs(send, recv, rc, 2, 7) == E.ERR_INVALID_ARGUMENT       # op
+    assert rs([base + 8, base + 16384], recv, rc, 2, 0) == E.ERR_INVALID_ARGUMENT   # alignment
+    # rank 1's send (2 blocks) overlaps rank 0's send
+    assert rs([base, base + 4096], recv, rc, 2, 0) == E.ERR_INVALID_ARGUMENT
+    # all-gather output (2 blocks) overlapping another rank's output
+    assert ag(send, [base + 32768, base + 36864], rc, 2) == E.ERR_INVALID_ARGUMENT
+    # in place is recognised, any other partial overlap is not
+    assert rs(send, [base + 4096, base + 16384], 0, 2, 0) == E.SUCCESS
+    assert rs(send, [base + 16, base + 16384 + 4096], rc, 2, 0) == E.ERR_INVALID_ARGUMENT
+    assert rs([base, base + 16384], [base + 16, base + 16384 + 4096 + 16], rc, 2, 0) == E.ERR_INVALID_ARGUMENT
+    # absurd counts
+    assert rs(send, recv, 1 << 60, 2, 0) == E.ERR_INVALID_ARGUMENT
+    assert ag(send, recv, 1 << 60, 2) == E.ERR_INVALID_ARGUMENT

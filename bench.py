@@ -28,9 +28,9 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "all-reduce busbw & HBM GB/s (% of peak) vs msg size, N virtual ranks, 1 GPU"
 WORKLOAD = "chain8_f32"
 LEGS = (("ring", "fused"), ("tree", "fused"), ("ring", "stepwise"), ("tree", "stepwise"))
-KERNEL_NAMES = {("ring", "fused"): "fused_allreduce (ring fold)",
-                ("tree", "fused"): "fused_allreduce (tree fold)",
-                ("ring", "stepwise"): "step_ring", ("tree", "stepwise"): "step_tree"}
+KERNEL_NAMES = {("ring", "fused"): "fused_collective (all-reduce, rotated ring fold)",
+                ("tree", "fused"): "fused_collective (all-reduce, rotated chain fold)",
+                ("ring", "stepwise"): "step_ring (all-reduce)", ("tree", "stepwise"): "step_tree"}
 KERNEL_SOURCES = ("double_binary_tree_amd/csrc/fused.hip", "double_binary_tree_amd/csrc/stepwise.hip",
                   "double_binary_tree_amd/csrc/device_ops.h", "double_binary_tree_amd/csrc/common.h")
 

@@ -23,7 +23,7 @@ hipError_t launch_fused(Coll coll, DType t, Op op, int mode, const FusedArgs& a,
 int fused_tile_vectors();
 hipError_t launch_stepwise(Coll coll, bool ring, DType t, Op op, const StepArgs& a, int grid, int block,
                            size_t lds, hipStream_t s);
-int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds);
+int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds, int group);
 int stepwise_vectors_per_lane(bool ring);
 
 namespace {
@@ -144,7 +144,7 @@ int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op,
   if (ring) {
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
-    std::vector<uint8_t> orders;
+    std::vector<uint32_t> orders;
     // cell index is 32-bit
     const uint64_t span = coll == kAllReduce ? count : count * (uint64_t)n;
     if (span / slice_elems >= ((uint64_t)1 << 32)) return EMU_ERR_INVALID_ARGUMENT;
@@ -155,11 +155,11 @@ int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op,
     p->ntasks = (uint32_t)tasks.size();
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
     if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
-    if (int e = p->orders.upload(orders.data(), orders.size())) return e;
+    if (int e = p->orders.upload(orders.data(), orders.size() * sizeof(uint32_t))) return e;
   } else {
     // One pipeline per resident workgroup (tasks per CU = occupancy, or the
     // tuning override EMU_TREE_TASKS_PER_CU).
-    const int occ_t = stepwise_occupancy(false, t, op, p->block, p->lds);
+    const int occ_t = stepwise_occupancy(false, t, op, p->block, p->lds, p->group);
     const long per_cu = env_long("EMU_TREE_TASKS_PER_CU", occ_t);
     std::vector<TreeTask> tasks;
     std::vector<TreeNode> nodes;
@@ -171,7 +171,7 @@ int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op,
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(TreeTask))) return e;
     if (int e = p->table.upload(nodes.data(), nodes.size() * sizeof(TreeNode))) return e;
   }
-  const int occ = stepwise_occupancy(ring, t, op, p->block, p->lds);
+  const int occ = stepwise_occupancy(ring, t, op, p->block, p->lds, p->group);
   p->grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntasks, (uint64_t)cus * occ));
   return EMU_SUCCESS;
 }
@@ -321,7 +321,7 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     for (int r = 0; r < n; ++r) { a.send[r] = sendbufs[r]; a.recv[r] = recvbufs[r]; }
     a.tasks = p.tasks.ptr;
     a.table = p.table.ptr;
-    a.orders = static_cast<const uint8_t*>(p.orders.ptr);
+    a.orders = static_cast<const uint32_t*>(p.orders.ptr);
     a.count = count;
     a.block = count;
     a.ntasks = p.ntasks;

@@ -87,7 +87,7 @@ struct TreeTask {
   uint32_t channel;   // a channel of the task's tree
 };
 // Tree record of one rank in one channel, plus its distance from the root.
-struct TreeNode {
+struct alignas(8) TreeNode {   // 8-byte aligned: one scalar load per record
   int8_t up;
   int8_t down[3];
   int8_t depth;
@@ -100,7 +100,7 @@ struct StepArgs {
   void* recv[kMaxRanks];
   const void* tasks;          // RingTask* or TreeTask*
   const void* table;          // RingLoopBlock* (ring) or TreeNode* (tree, [nch][nranks])
-  const uint8_t* orders;      // ring: [rings][kMaxRanks], position p -> rank
+  const uint32_t* orders;     // ring: [rings][kMaxRanks], position p -> rank
   uint64_t count;             // elements per rank
   uint64_t block;             // reduce-scatter / all-gather: elements per block
   uint32_t ntasks;

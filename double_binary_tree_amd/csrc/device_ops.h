@@ -150,6 +150,20 @@ struct Unit {
 #ifndef EMU_STORE_NT
 #define EMU_STORE_NT 1
 #endif
+// Raw buffer view starting at `base` (wave-uniform).  The hardware returns
+// zeros for any offset at or past its range, so a lane that must not read
+// passes kNoLoad instead of branching around the load.
+constexpr uint32_t kBufRange = 0x7FFFFFF0u;
+constexpr uint32_t kNoLoad = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kBufRange,
+                                           0x00020000 /* 32-bit data format */);
+}
+__device__ __forceinline__ u32x4 ld_buf(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)byte_off, 0,
+                                                                         EMU_LOAD_NT ? 2 /* nt */ : 0));
+}
+
 __device__ __forceinline__ u32x4 ld_vec(const void* base, uint64_t byte_off) {
   const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off);
 #if EMU_LOAD_NT

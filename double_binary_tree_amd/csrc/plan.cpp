@@ -133,13 +133,13 @@ void build_fused_coll_tiles(const Topology& topo, Coll coll, const FusedOrders& 
 
 void build_ring_coll_tasks(const Topology& topo, uint64_t block, uint64_t unit, uint64_t chunk_count,
                            uint64_t slice_elems, std::vector<RingLoopBlock>* loops, std::vector<RingTask>* tasks,
-                           std::vector<uint8_t>* orders) {
+                           std::vector<uint32_t>* orders) {
   const int n = topo.nranks;
   loops->clear();
   tasks->clear();
   orders->assign((size_t)topo.nrings * kMaxRanks, 0);
   for (const ChannelTopology& c : topo.channels)
-    for (int p = 0; p < n; ++p) (*orders)[(size_t)c.ring_id * kMaxRanks + p] = (uint8_t)c.order[p];
+    for (int p = 0; p < n; ++p) (*orders)[(size_t)c.ring_id * kMaxRanks + p] = (uint32_t)c.order[p];
   uint32_t loop_id = 0;
   const std::vector<Range> chans = channel_ranges(block, unit, topo.nchannels);
   for (int c = 0; c < topo.nchannels; ++c) {
@@ -337,12 +337,12 @@ int compile_tree_program(const ChannelTopology& ch, uint8_t perm[kMaxRanks],
 
 void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,
                       uint64_t slice_elems, std::vector<RingLoopBlock>* loops,
-                      std::vector<RingTask>* tasks, std::vector<uint8_t>* orders) {
+                      std::vector<RingTask>* tasks, std::vector<uint32_t>* orders) {
   loops->clear();
   tasks->clear();
   orders->assign((size_t)topo.nrings * kMaxRanks, 0);
   for (const ChannelTopology& c : topo.channels)
-    for (int p = 0; p < topo.nranks; ++p) (*orders)[(size_t)c.ring_id * kMaxRanks + p] = (uint8_t)c.order[p];
+    for (int p = 0; p < topo.nranks; ++p) (*orders)[(size_t)c.ring_id * kMaxRanks + p] = (uint32_t)c.order[p];
   uint32_t loop_id = 0;
   const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
   for (int c = 0; c < topo.nchannels; ++c) {

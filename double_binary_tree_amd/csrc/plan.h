@@ -61,13 +61,13 @@ void build_fused_coll_tiles(const Topology& topo, Coll coll, const FusedOrders& 
 // block).  Loop table, tasks and ring orders as for build_ring_tasks.
 void build_ring_coll_tasks(const Topology& topo, uint64_t block, uint64_t unit, uint64_t chunk_count,
                            uint64_t slice_elems, std::vector<RingLoopBlock>* loops, std::vector<RingTask>* tasks,
-                           std::vector<uint8_t>* orders);
+                           std::vector<uint32_t>* orders);
 
 // Stepwise ring: loop table (nranks blocks per loop), tasks (loop, slice,
 // ring order) and the ring order table ([nrings][kMaxRanks]).
 void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count,
                       uint64_t slice_elems, std::vector<RingLoopBlock>* loops,
-                      std::vector<RingTask>* tasks, std::vector<uint8_t>* orders);
+                      std::vector<RingTask>* tasks, std::vector<uint32_t>* orders);
 
 // Stepwise tree: about target_tasks contiguous pieces of the message, each
 // inside one run of channels with the same tree records and cut at

@@ -23,6 +23,8 @@
 // broadcasts slice q at stage q + H + d; the root writes the result at its
 // reduce stage.  Reduce-up and broadcast-down run concurrently on different
 // slices, with separate slot sets, as the split thread groups of the pages do.
+#include <algorithm>
+
 #include "device_ops.h"
 
 namespace emu {
@@ -47,11 +49,18 @@ __device__ __forceinline__ void step_barrier() {
 #ifndef EMU_RING_PREFETCH
 #define EMU_RING_PREFETCH 2
 #endif
+
+#ifndef EMU_RING_PREFETCH_WAVE
+#define EMU_RING_PREFETCH_WAVE 2
+#endif
 #ifndef EMU_TREE_VPT
 #define EMU_TREE_VPT 1
 #endif
 #ifndef EMU_TREE_PREFETCH
 #define EMU_TREE_PREFETCH 1
+#endif
+#ifndef EMU_TREE_PREFETCH_WAVE
+#define EMU_TREE_PREFETCH_WAVE 3
 #endif
 
 // COLL selects the collective: the all-reduce runs both halves; the
@@ -59,31 +68,57 @@ __device__ __forceinline__ void step_barrier() {
 // finished block (the position's own block) to its rank's output, one
 // block lower; the standalone all-gather starts from each position's own
 // input (one block lower) and runs only the N-1 forwarding steps.
-template <typename R, int ESZ, int COLL>
-__global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
+//
+// WAVE: the group is one wave (G = 64), so the position, its rank and every
+// block descriptor are wave-uniform; they are moved to scalar registers and
+// only the lane's place in the slice stays per lane.
+//
+// The task and record tables come as their own read-only arguments: uniform
+// reads from them then go through the scalar unit, whose counter is separate
+// from the vector-memory counter; a vector load there would make the wait
+// for it also wait for every store issued before it.
+template <bool WAVE>
+__device__ __forceinline__ uint32_t wave_u32(uint32_t x) {
+  if constexpr (WAVE) return __builtin_amdgcn_readfirstlane(x);
+  return x;
+}
+template <bool WAVE>
+__device__ __forceinline__ uint64_t wave_u64(uint64_t x) {
+  if constexpr (WAVE)
+    return (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)x) |
+           (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32;
+  return x;
+}
+
+template <typename R, int ESZ, int COLL, bool WAVE>
+__global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTask* __restrict__ tasks,
+                                                   const RingLoopBlock* __restrict__ loops,
+                                                   const uint32_t* __restrict__ orders) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_RING_VPT;
-  constexpr int kPrefetch = EMU_RING_PREFETCH;
+  constexpr int kPrefetch = WAVE ? EMU_RING_PREFETCH_WAVE : EMU_RING_PREFETCH;
   extern __shared__ u32x4 fifo[];   // slots [2][N][V][G], descriptors [2][N], ring orders [2][kMaxRanks] bytes
-  const uint32_t n = a.nranks, g = a.group;
-  const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;   // r: ring position
+  const uint32_t n = a.nranks, g = WAVE ? 64u : a.group;
+  // r: ring position
+  const uint32_t r = WAVE ? wave_u32<WAVE>(threadIdx.x / 64u) : threadIdx.x / g;
+  const uint32_t p = WAVE ? threadIdx.x % 64u : threadIdx.x % g;
   const bool active = r < n;
   const uint32_t prev = active ? (r + n - 1) % n : 0;
-  const RingLoopBlock* loops = static_cast<const RingLoopBlock*>(a.table);
-  const RingTask* tasks = static_cast<const RingTask*>(a.tasks);
   auto slot = [&](uint32_t parity, uint32_t rank, int v) -> u32x4& {
     return fifo[((parity * n + rank) * V + v) * g + p];
   };
   // Block descriptors of the current and the next task, staged in LDS (two
   // sets) so that no step waits on a descriptor load: the next task's are
-  // copied during the current task's first step.
+  // copied during the current task's first step.  (Measured on MI355X:
+  // staging with per-wave scalar loads, or a queue unrolled to rotate by
+  // name as the tree does, were each about 15% slower here.)
   RingLoopBlock* desc = reinterpret_cast<RingLoopBlock*>(fifo + 2 * (size_t)n * V * g);   // [2][N]
   uint8_t* order = reinterpret_cast<uint8_t*>(desc + 2 * n);                                // [2][kMaxRanks]
   auto stage_desc = [&](uint32_t t, uint32_t set) {
     if (t < a.ntasks && threadIdx.x < n) {
       const RingTask tk = tasks[t];
       desc[set * n + threadIdx.x] = loops[(size_t)tk.loop * n + threadIdx.x];
-      order[set * kMaxRanks + threadIdx.x] = a.orders[(size_t)tk.ring * kMaxRanks + threadIdx.x];
+      order[set * kMaxRanks + threadIdx.x] = (uint8_t)orders[(size_t)tk.ring * kMaxRanks + threadIdx.x];
     }
   };
   stage_desc(blockIdx.x, 0);
@@ -93,7 +128,8 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x, set ^= 1) {
     const RingTask task = tasks[t];
     const RingLoopBlock* blk = desc + set * n;
-    const uint32_t me = active ? order[set * kMaxRanks + r] : 0;   // the rank at position r
+    // the rank at position r
+    const uint32_t me = active ? wave_u32<WAVE>(order[set * kMaxRanks + r]) : 0;
     // byte distance between a block's place and the rank's own buffer
     const uint64_t my_shift = COLL == kAllReduce ? 0 : (uint64_t)me * a.block * ESZ;
     const uint64_t load_shift = COLL == kAllGather ? my_shift : 0;
@@ -103,35 +139,70 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
     // grid that the block overlaps; lane p's vector v sits at a fixed place in
     // the cell (aligned accesses), and is live only inside the block.
     const uint64_t slice_elems = (uint64_t)V * g * unit;
-    auto pos_of = [&](uint32_t b, int v) -> uint64_t {
-      return ((uint64_t)blk[b].first_cell + task.slice) * slice_elems + ((uint64_t)v * g + p) * unit;
+    // Block b as seen by this task: the first element of its slice cell and
+    // its [start, end) range (wave-uniform under WAVE).
+    struct View { uint64_t cell, start, end; };
+    auto view_of = [&](uint32_t b) -> View {
+      const RingLoopBlock d = blk[b];
+      const uint64_t start = wave_u64<WAVE>(d.offset);
+      const uint32_t nelem = wave_u32<WAVE>(d.nelem), first = wave_u32<WAVE>(d.first_cell);
+      return {((uint64_t)first + task.slice) * slice_elems, start, start + nelem};
     };
-    auto nbytes_of = [&](uint32_t b, int v) -> int {
-      const uint64_t pos = pos_of(b, v), start = blk[b].offset, end = start + blk[b].nelem;
-      if (pos < start || pos >= end) return 0;
-      const uint64_t left = end - pos;
+    auto nbytes_of = [&](const View& w, uint64_t pos) -> int {
+      if (pos < w.start || pos >= w.end) return 0;
+      const uint64_t left = w.end - pos;
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
-    auto boff_of = [&](uint32_t b, int v) -> uint64_t { return pos_of(b, v) * ESZ; };
-    auto load_block = [&](uint32_t b, u32x4 (&x)[V]) {
+    // Under WAVE a block is read with one buffer view based at its slice
+    // cell: whole vectors load without a branch (other lanes read zeros, the
+    // hardware range check), and a partial vector at the message end is read
+    // when it is consumed (fix_block).
+    auto load_block = [&](uint32_t b, u32x4 (&x)[V], bool enable) {
+      const View w = view_of(b);
+      const void* src = a.send[me];
+      if constexpr (WAVE) {
+        const auto rs = buffer_view(static_cast<const char*>(src) + (w.cell * ESZ - load_shift));
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int nb = nbytes_of(b, v);
-        x[v] = nb ? ld_any(a.send[me], boff_of(b, v) - load_shift, nb) : u32x4{0, 0, 0, 0};
+        for (int v = 0; v < V; ++v) {
+          const uint32_t lane = (uint32_t)((v * g + p) * unit);
+          x[v] = ld_buf(rs, enable && nbytes_of(w, w.cell + lane) == kVecBytes ? lane * ESZ : kNoLoad);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
+          const int nb = enable ? nbytes_of(w, pos) : 0;
+          x[v] = nb ? ld_any(src, pos * ESZ - load_shift, nb) : u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    auto fix_block = [&](uint32_t b, u32x4 (&x)[V]) {
+      if constexpr (WAVE) {
+        const View w = view_of(b);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
+          const int nb = nbytes_of(w, pos);
+          if (nb > 0 && nb < kVecBytes) x[v] = ld_part(a.send[me], pos * ESZ - load_shift, nb);
+        }
       }
     };
     auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
+      const View w = view_of(b);
+      void* dst = a.recv[me];
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const int nb = nbytes_of(b, v);
-        if (nb) st_any(a.recv[me], boff_of(b, v) - store_shift, nb, R::post(x[v]));
+        const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
+        const int nb = nbytes_of(w, pos);
+        if (nb) st_any(dst, pos * ESZ - store_shift, nb, R::post(x[v]));
       }
     };
 
     if (n == 1) {
       if (active) {
         u32x4 x[V];
-        load_block(0, x);
+        load_block(0, x, true);
+        fix_block(0, x);
         store_block(0, x);
       }
       // one rank: no steps, so stage the next descriptor here
@@ -145,7 +216,8 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
       // to its own output and into the slot the forwarding steps read first
       if (active) {
         u32x4 own[V];
-        load_block((r + 1) % n, own);
+        load_block((r + 1) % n, own, true);
+        fix_block((r + 1) % n, own);
         store_block((r + 1) % n, own);
 #pragma unroll
         for (int v = 0; v < V; ++v) slot((n - 1) & 1, r, v) = R::pre(own[v]);
@@ -156,16 +228,15 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
     // (queue q[0] is the next step's block).
     u32x4 own[V], q[kPrefetch][V];
     if (active) {
-      load_block(r, own);
+      load_block(r, own, true);
 #pragma unroll
       for (int i = 0; i < kPrefetch; ++i)
-        if ((uint32_t)i + 1 < n) load_block((r + 2 * n - 1 - i) % n, q[i]);
+        if ((uint32_t)i + 1 < n) load_block((r + 2 * n - 1 - i) % n, q[i], true);
+      fix_block(r, own);
 #pragma unroll
       for (int v = 0; v < V; ++v) slot(0, r, v) = R::pre(own[v]);
     }
     step_barrier();
-
-    // reduce-scatter steps 1..N-1
     for (uint32_t s = 1; s < n; ++s) {
       const uint32_t b = (r + n - s) % n;
       if (active) {
@@ -176,7 +247,8 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
         for (int i = 0; i + 1 < kPrefetch; ++i)
 #pragma unroll
           for (int v = 0; v < V; ++v) q[i][v] = q[i + 1][v];
-        if (s + kPrefetch < n) load_block((r + 2 * n - s - kPrefetch) % n, q[kPrefetch - 1]);
+        if (s + kPrefetch < n) load_block((r + 2 * n - s - kPrefetch) % n, q[kPrefetch - 1], true);
+        fix_block(b, mine);
         u32x4 res[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) res[v] = R::op(R::pre(mine[v]), slot((s - 1) & 1, prev, v));
@@ -208,17 +280,19 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a) {
 
 // ---------------------------------------------------------------------------
 // Tree.
-template <typename R, int ESZ>
-__global__ __launch_bounds__(1024) void step_tree(const StepArgs a) {
+// WAVE as for the ring: one wave per rank, rank and tree record in scalar
+// registers.
+template <typename R, int ESZ, bool WAVE>
+__global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTask* __restrict__ tasks,
+                                                   const TreeNode* __restrict__ nodes) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_TREE_VPT;
-  constexpr int kPrefetch = EMU_TREE_PREFETCH;
+  constexpr int kPrefetch = WAVE ? EMU_TREE_PREFETCH_WAVE : EMU_TREE_PREFETCH;
   extern __shared__ u32x4 fifo[];   // up[2][N][V][G] then down[2][N][V][G]
-  const uint32_t n = a.nranks, g = a.group;
-  const uint32_t r = threadIdx.x / g, p = threadIdx.x % g;
+  const uint32_t n = a.nranks, g = WAVE ? 64u : a.group;
+  const uint32_t r = WAVE ? wave_u32<WAVE>(threadIdx.x / 64u) : threadIdx.x / g;
+  const uint32_t p = WAVE ? threadIdx.x % 64u : threadIdx.x % g;
   const bool active = r < n;
-  const TreeTask* tasks = static_cast<const TreeTask*>(a.tasks);
-  const TreeNode* nodes = static_cast<const TreeNode*>(a.table);
   const int H = (int)a.height;
   const uint32_t slice_elems = V * g * unit;
   auto up_slot = [&](int parity, uint32_t rank, int v) -> u32x4& {
@@ -230,8 +304,12 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a) {
 
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x) {
     const TreeTask task = tasks[t];
-    const TreeNode me = nodes[(size_t)task.channel * n + (active ? r : 0)];
-    const int depth = me.depth;
+    const TreeNode rec = nodes[wave_u32<WAVE>(task.channel * n + (active ? r : 0))];
+    struct { int up, down[3]; } me;
+    me.up = (int)wave_u32<WAVE>((uint32_t)(int)rec.up);
+#pragma unroll
+    for (int s = 0; s < 3; ++s) me.down[s] = (int)wave_u32<WAVE>((uint32_t)(int)rec.down[s]);
+    const int depth = (int)wave_u32<WAVE>((uint32_t)(int)rec.depth);
     const bool is_root = me.up < 0;
     const bool has_children = me.down[0] >= 0;
     // Slices are the slice-size cells of the global element grid that the
@@ -249,11 +327,33 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a) {
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
     auto boff_of = [&](int q, int v) -> uint64_t { return pos_of(q, v) * ESZ; };
-    auto load_slice = [&](int q, u32x4 (&x)[V]) {
+    // Under WAVE a slice is read with a buffer view based at its cell (whole
+    // vectors without a branch, other lanes read zeros) and a partial vector
+    // at the task end is read when it is consumed (fix_slice), as in the ring.
+    auto load_slice = [&](int q, u32x4 (&x)[V], bool enable) {
+      if constexpr (WAVE) {
+        const auto rs = buffer_view(static_cast<const char*>(a.send[r]) + pos_of(q, 0) * ESZ -
+                                    (uint64_t)p * kVecBytes);
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int nb = nbytes_of(q, v);
-        x[v] = nb ? ld_any(a.send[r], boff_of(q, v), nb) : u32x4{0, 0, 0, 0};
+        for (int v = 0; v < V; ++v) {
+          const uint32_t lane = (uint32_t)((v * g + p) * kVecBytes);
+          x[v] = ld_buf(rs, enable && nbytes_of(q, v) == kVecBytes ? lane : kNoLoad);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int nb = enable ? nbytes_of(q, v) : 0;
+          x[v] = nb ? ld_any(a.send[r], boff_of(q, v), nb) : u32x4{0, 0, 0, 0};
+        }
+      }
+    };
+    auto fix_slice = [&](int q, u32x4 (&x)[V]) {
+      if constexpr (WAVE) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          const int nb = nbytes_of(q, v);
+          if (nb > 0 && nb < kVecBytes) x[v] = ld_part(a.send[r], boff_of(q, v), nb);
+        }
       }
     };
     auto store_slice = [&](int q, const u32x4 (&x)[V]) {
@@ -267,57 +367,70 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a) {
     const int dn_lag = H + depth;        // broadcast slice q at stage q + dn_lag
     const int nstages = nslices + 2 * H;
 
-    // own inputs of the next kPrefetch reduce slices are loaded ahead
-    // (queue q[0] is the next one).
+    // The own input of reduce slice q is loaded PF stages ahead into queue
+    // entry q mod PF.  The stage loop is unrolled by PF with a per-wave
+    // phase (stage st0 + i reduces a slice = i mod PF), and every entry is
+    // refilled unconditionally (a load of nothing when there is no slice),
+    // so entries rotate by name and are never merged or copied while their
+    // loads are in flight.  Stages before 0 only refill; every wave still
+    // meets the barriers of stages 0 .. nstages-1 in order.  Without WAVE a
+    // wave may hold several ranks with different lags, so the queue is one
+    // entry deep and the phase is 0 for all.
+    static_assert(WAVE || kPrefetch == 1, "a multi-rank wave needs a one-entry queue");
+    const int ph = ((up_lag % kPrefetch) + kPrefetch) % kPrefetch;
     u32x4 q[kPrefetch][V];
-    if (active) {
+    for (int st0 = ph - kPrefetch; st0 < nstages; st0 += kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < kPrefetch; ++i)
-        if (i < nslices) load_slice(i, q[i]);
-    }
-    for (int st = 0; st < nstages; ++st) {
-      const int cur = st & 1, prv = cur ^ 1;
-      const int qu = st - up_lag;
-      if (active && qu >= 0 && qu < nslices) {
-        u32x4 acc[V];
+      for (int i = 0; i < kPrefetch; ++i) {
+        const int st = st0 + i;
+        const bool live = st >= 0 && st < nstages;
+        const int cur = st & 1, prv = cur ^ 1;
+        const int qu = st - up_lag;
+        if (live && active && qu >= 0 && qu < nslices) {
+          u32x4 acc[V];
 #pragma unroll
-        for (int v = 0; v < V; ++v) acc[v] = R::pre(q[0][v]);
+          for (int v = 0; v < V; ++v) acc[v] = q[i][v];
+          fix_slice(qu, acc);
 #pragma unroll
-        for (int i = 0; i + 1 < kPrefetch; ++i)
+          for (int v = 0; v < V; ++v) acc[v] = R::pre(acc[v]);
 #pragma unroll
-          for (int v = 0; v < V; ++v) q[i][v] = q[i + 1][v];
-        if (qu + kPrefetch < nslices) load_slice(qu + kPrefetch, q[kPrefetch - 1]);
+          for (int s = 0; s < 3; ++s) {
+            const int c = me.down[s];
+            if (c >= 0) {
 #pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          const int c = me.down[s];
-          if (c >= 0) {
+              for (int v = 0; v < V; ++v) acc[v] = R::op(acc[v], up_slot(prv, (uint32_t)c, v));
+            }
+          }
+          if (is_root) {
+            store_slice(qu, acc);
+            if (has_children) {
 #pragma unroll
-            for (int v = 0; v < V; ++v) acc[v] = R::op(acc[v], up_slot(prv, (uint32_t)c, v));
+              for (int v = 0; v < V; ++v) dn_slot(cur, r, v) = acc[v];
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v) up_slot(cur, r, v) = acc[v];
           }
         }
-        if (is_root) {
-          store_slice(qu, acc);
-          if (has_children) {
+        {
+          const int qn = qu + kPrefetch;
+          load_slice(qn, q[i], active && qn >= 0 && qn < nslices);
+        }
+        if (live) {
+          const int qd = st - dn_lag;
+          if (active && !is_root && qd >= 0 && qd < nslices) {
+            u32x4 x[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) dn_slot(cur, r, v) = acc[v];
+            for (int v = 0; v < V; ++v) x[v] = dn_slot(prv, (uint32_t)me.up, v);
+            store_slice(qd, x);
+            if (has_children) {
+#pragma unroll
+              for (int v = 0; v < V; ++v) dn_slot(cur, r, v) = x[v];
+            }
           }
-        } else {
-#pragma unroll
-          for (int v = 0; v < V; ++v) up_slot(cur, r, v) = acc[v];
+          step_barrier();
         }
       }
-      const int qd = st - dn_lag;
-      if (active && !is_root && qd >= 0 && qd < nslices) {
-        u32x4 x[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) x[v] = dn_slot(prv, (uint32_t)me.up, v);
-        store_slice(qd, x);
-        if (has_children) {
-#pragma unroll
-          for (int v = 0; v < V; ++v) dn_slot(cur, r, v) = x[v];
-        }
-      }
-      step_barrier();
     }
   }
 }
@@ -330,17 +443,29 @@ static hipError_t allow_lds(K kernel, size_t lds) {
                              (int)lds);
 }
 
+template <DType T, Op O, int COLL, bool WAVE>
+static hipError_t launch_ring_w(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
+  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz, COLL, WAVE>, lds)) return e;
+  hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz, COLL, WAVE>), dim3(grid), dim3(block), lds, s, a,
+                     static_cast<const RingTask*>(a.tasks), static_cast<const RingLoopBlock*>(a.table), a.orders);
+  return hipGetLastError();
+}
 template <DType T, Op O, int COLL>
 static hipError_t launch_ring_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz, COLL>, lds)) return e;
-  hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz, COLL>), dim3(grid), dim3(block), lds, s, a);
+  return a.group == 64 ? launch_ring_w<T, O, COLL, true>(a, grid, block, lds, s)
+                       : launch_ring_w<T, O, COLL, false>(a, grid, block, lds, s);
+}
+template <DType T, Op O, bool WAVE>
+static hipError_t launch_tree_w(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
+  if (hipError_t e = allow_lds(step_tree<Red<T, O>, Unit<T>::esz, WAVE>, lds)) return e;
+  hipLaunchKernelGGL((step_tree<Red<T, O>, Unit<T>::esz, WAVE>), dim3(grid), dim3(block), lds, s, a,
+                     static_cast<const TreeTask*>(a.tasks), static_cast<const TreeNode*>(a.table));
   return hipGetLastError();
 }
 template <DType T, Op O>
 static hipError_t launch_tree_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  if (hipError_t e = allow_lds(step_tree<Red<T, O>, Unit<T>::esz>, lds)) return e;
-  hipLaunchKernelGGL((step_tree<Red<T, O>, Unit<T>::esz>), dim3(grid), dim3(block), lds, s, a);
-  return hipGetLastError();
+  return a.group == 64 ? launch_tree_w<T, O, true>(a, grid, block, lds, s)
+                       : launch_tree_w<T, O, false>(a, grid, block, lds, s);
 }
 
 template <DType T>
@@ -387,26 +512,30 @@ static int occupancy_of(K kernel, int block, size_t lds) {
 }
 
 template <DType T, Op O>
-static int occupancy_t(bool ring, int block, size_t lds) {
-  return ring ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce>, block, lds)
-              : occupancy_of(step_tree<Red<T, O>, Unit<T>::esz>, block, lds);
+static int occupancy_t(bool ring, bool wave, int block, size_t lds) {
+  if (!ring)
+    return wave ? occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, true>, block, lds)
+                : occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, false>, block, lds);
+  return wave ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, true>, block, lds)
+              : occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, false>, block, lds);
 }
 
 // Resident workgroups per CU for the stepwise kernels at this block/LDS size
-// (the ring all-reduce kernel stands for its reduce-scatter and all-gather
-// forms, which use no more registers).
-int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds) {
+// and group (64 lanes: the one-wave-per-rank variant).  The ring all-reduce
+// kernel stands for its reduce-scatter and all-gather forms.
+int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds, int group) {
+  const bool wave = group == 64;
   switch (t) {
-    case DType::I32: return op == Op::Sum ? occupancy_t<DType::I32, Op::Sum>(ring, block, lds)
-                                          : occupancy_t<DType::I32, Op::Max>(ring, block, lds);
-    case DType::I64: return op == Op::Sum ? occupancy_t<DType::I64, Op::Sum>(ring, block, lds)
-                                          : occupancy_t<DType::I64, Op::Max>(ring, block, lds);
-    case DType::F32: return op == Op::Sum ? occupancy_t<DType::F32, Op::Sum>(ring, block, lds)
-                                          : occupancy_t<DType::F32, Op::Max>(ring, block, lds);
-    case DType::F16: return op == Op::Sum ? occupancy_t<DType::F16, Op::Sum>(ring, block, lds)
-                                          : occupancy_t<DType::F16, Op::Max>(ring, block, lds);
-    case DType::BF16: return op == Op::Sum ? occupancy_t<DType::BF16, Op::Sum>(ring, block, lds)
-                                           : occupancy_t<DType::BF16, Op::Max>(ring, block, lds);
+    case DType::I32: return op == Op::Sum ? occupancy_t<DType::I32, Op::Sum>(ring, wave, block, lds)
+                                          : occupancy_t<DType::I32, Op::Max>(ring, wave, block, lds);
+    case DType::I64: return op == Op::Sum ? occupancy_t<DType::I64, Op::Sum>(ring, wave, block, lds)
+                                          : occupancy_t<DType::I64, Op::Max>(ring, wave, block, lds);
+    case DType::F32: return op == Op::Sum ? occupancy_t<DType::F32, Op::Sum>(ring, wave, block, lds)
+                                          : occupancy_t<DType::F32, Op::Max>(ring, wave, block, lds);
+    case DType::F16: return op == Op::Sum ? occupancy_t<DType::F16, Op::Sum>(ring, wave, block, lds)
+                                          : occupancy_t<DType::F16, Op::Max>(ring, wave, block, lds);
+    case DType::BF16: return op == Op::Sum ? occupancy_t<DType::BF16, Op::Sum>(ring, wave, block, lds)
+                                           : occupancy_t<DType::BF16, Op::Max>(ring, wave, block, lds);
   }
   return 1;
 }

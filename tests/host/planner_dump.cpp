@@ -87,7 +87,7 @@ int main(int argc, char** argv) {
     }
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
-    std::vector<uint8_t> orders;
+    std::vector<uint32_t> orders;
     const uint64_t slice = 64 * unit;
     build_ring_coll_tasks(topo, block, unit, chunk, slice, &loops, &tasks, &orders);
     std::printf("\"coll_block\": %llu, \"coll_blocks\": [", (unsigned long long)block);
@@ -105,7 +105,7 @@ int main(int argc, char** argv) {
   {
     std::vector<RingLoopBlock> loops;
     std::vector<RingTask> tasks;
-    std::vector<uint8_t> orders;
+    std::vector<uint32_t> orders;
     const uint64_t slice = 64 * unit;
     build_ring_tasks(topo, count, unit, chunk, slice, &loops, &tasks, &orders);
     std::printf("\"ring_slice\": %llu, \"ring_blocks\": [", (unsigned long long)slice);

@@ -62,14 +62,15 @@ struct Plan {
 
 struct Comm {
   int nranks = 0, nnodes = 0, nchannels = 0;
-  Algo algo = Algo::Ring;
+  Algo algo = Algo::Ring;     // the fixed algorithm, or the ring for reduce-scatter / all-gather
+  bool auto_algo = false;     // EMU_ALGO_AUTO: ring or tree per call, by the cost model
   bool fused = false;
   size_t chunk_bytes = 0;
   Topology topo;
-  FusedOrders orders;        // fused all-reduce: how each tile names its order
-  FusedOrders ring_orders;   // fused reduce-scatter: the ring orders (any algo)
-  // (device, count, dtype, op, collective) -> plan
-  std::map<std::tuple<int, uint64_t, int, int, int>, std::unique_ptr<Plan>> plans;
+  FusedOrders ring_orders;   // fused ring all-reduce and reduce-scatter: how each tile names its order
+  FusedOrders tree_orders;   // fused tree all-reduce (built when the tree may run)
+  // (device, count, dtype, op, collective, algo) -> plan
+  std::map<std::tuple<int, uint64_t, int, int, int, int>, std::unique_ptr<Plan>> plans;
 };
 
 using CommKey = std::tuple<int, int, int, int, size_t, int, std::vector<int>>;
@@ -102,7 +103,7 @@ int cu_count(int dev) {
 
 // `count` is the elements per rank of the all-reduce, or the block size of
 // the reduce-scatter / all-gather.
-int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op, Plan* p) {
+int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, Op op, Plan* p) {
   const int esz = elem_size(t);
   const uint64_t unit = kVecBytes / esz;
   const uint64_t chunk_count = c.chunk_bytes / esz;
@@ -110,9 +111,9 @@ int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op,
   if (c.fused) {
     std::vector<Tile> tiles;
     const uint64_t tile_elems = (uint64_t)fused_tile_vectors() * unit;
-    const FusedOrders& ord = coll == kAllReduce ? c.orders : c.ring_orders;
+    const FusedOrders& ord = algo == Algo::Ring ? c.ring_orders : c.tree_orders;
     if (coll == kAllReduce)
-      build_fused_tiles(c.topo, c.algo, ord, count, unit, chunk_count, tile_elems, &tiles);
+      build_fused_tiles(c.topo, algo, ord, count, unit, chunk_count, tile_elems, &tiles);
     else
       build_fused_coll_tiles(c.topo, coll, ord, count, unit, tile_elems, &tiles);
     p->ntiles = (uint32_t)tiles.size();
@@ -123,7 +124,7 @@ int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op,
     return EMU_SUCCESS;
   }
   const int n = c.nranks;
-  const bool ring = c.algo == Algo::Ring || coll != kAllReduce;
+  const bool ring = algo == Algo::Ring;
   const int vpl = stepwise_vectors_per_lane(ring);
   // Lanes per virtual rank: the widest group that fits one workgroup
   // (N*G <= 1024 threads) and the device's LDS per workgroup.
@@ -176,6 +177,34 @@ int make_plan(const Comm& c, Coll coll, int dev, uint64_t count, DType t, Op op,
   return EMU_SUCCESS;
 }
 
+// Cost model (page "NCCL 专家课程 13", section "理想成本模型"; page "all-reduce
+// 每张卡要发多少数据?", section "α–β 模型"): per mode and algorithm, alpha
+// (us per dependent stage, the fixed cost of a call folded in) and the
+// bandwidth B (bytes/us).  Predicted time of S bytes per rank:
+//   ring 2(N-1)*alpha + 2(N-1)/N * S/B,   tree 2*D*alpha + 2*S/B,
+// D the deepest channel tree.  Defaults: least-squares fit to the 12-channel
+// message-size sweep of 8 ranks on one node measured on MI355X.
+struct Cost { double alpha_us, bw; };
+Cost g_cost[2][2] = {          // [stepwise, fused][ring, tree]
+    {{1.09866, 646291.0}, {1.05829, 655217.0}},
+    {{0.619739, 635033.0}, {0.596203, 748673.0}},
+};
+
+double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {
+  const Cost& k = g_cost[fused ? 1 : 0][algo == Algo::Ring ? 0 : 1];
+  const int n = c.nranks;
+  if (algo == Algo::Ring) return (double)(2 * (n - 1)) * k.alpha_us + 2.0 * (n - 1) / n * nbytes / k.bw;
+  int depth = 0;
+  for (const auto& ch : c.topo.channels) depth = std::max(depth, ch.height);
+  return (double)(2 * depth) * k.alpha_us + 2.0 * nbytes / k.bw;
+}
+
+// The smaller predicted time; the ring on an exact tie.
+Algo select_algo(const Comm& c, double nbytes) {
+  return predict_us(c, c.fused, Algo::Tree, nbytes) < predict_us(c, c.fused, Algo::Ring, nbytes) ? Algo::Tree
+                                                                                                  : Algo::Ring;
+}
+
 bool valid_dtype(int d) { return d >= EMU_INT32 && d <= EMU_BFLOAT16; }
 bool valid_op(int o) { return o == EMU_SUM || o == EMU_MAX; }
 
@@ -190,7 +219,7 @@ int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t 
                         const int* intra) {
   const int base = algo & 0xFF;
   const int mode = algo & ~0xFF;
-  if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE) return EMU_ERR_INVALID_ARGUMENT;
+  if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE && base != EMU_ALGO_AUTO) return EMU_ERR_INVALID_ARGUMENT;
   if (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED) return EMU_ERR_INVALID_ARGUMENT;
   if (chunk_bytes == 0 || chunk_bytes % kVecBytes != 0 || chunk_bytes > ((size_t)1 << 30))
     return EMU_ERR_INVALID_ARGUMENT;
@@ -211,12 +240,14 @@ int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t 
   c->nranks = nranks;
   c->nnodes = nnodes;
   c->nchannels = nchannels;
-  c->algo = base == EMU_ALGO_RING ? Algo::Ring : Algo::Tree;
+  c->algo = base == EMU_ALGO_TREE ? Algo::Tree : Algo::Ring;
+  c->auto_algo = base == EMU_ALGO_AUTO;
   c->fused = mode == EMU_MODE_FUSED;
   c->chunk_bytes = chunk_bytes;
   if (int e = build_topology(nranks, nnodes, nchannels, pattern, order.data(), &c->topo)) return e;
-  if (int e = build_fused_orders(c->topo, c->algo, &c->orders)) return e;
   if (int e = build_fused_orders(c->topo, Algo::Ring, &c->ring_orders)) return e;
+  if (base != EMU_ALGO_RING)
+    if (int e = build_fused_orders(c->topo, Algo::Tree, &c->tree_orders)) return e;
   if (g_comms.size() >= kMaxCachedComms) {
     // Drop every cached communicator except the active one.  Their device
     // tables may still be read by enqueued kernels: wait for the device first.
@@ -291,12 +322,16 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
+  const Algo algo = coll != kAllReduce ? Algo::Ring
+                    : c->auto_algo      ? select_algo(*c, (double)count * (double)esz)
+                                        : c->algo;
   const int op_key = (c->fused && coll == kAllReduce) || coll == kAllGather ? 0 : op;
-  const auto key = std::make_tuple(dev, (uint64_t)count, coll == kAllGather ? elem_size(t) : dtype, op_key, (int)coll);
+  const auto key = std::make_tuple(dev, (uint64_t)count, coll == kAllGather ? elem_size(t) : dtype, op_key, (int)coll,
+                                   (int)algo);
   auto it = c->plans.find(key);
   if (it == c->plans.end()) {
     auto p = std::make_unique<Plan>();
-    if (int e = make_plan(*c, coll, dev, count, t, o, p.get())) return e;
+    if (int e = make_plan(*c, coll, algo, dev, count, t, o, p.get())) return e;
     it = c->plans.emplace(key, std::move(p)).first;
   }
   const Plan& p = *it->second;
@@ -304,7 +339,7 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
   hipError_t err;
   if (c->fused) {
     FusedArgs a{};
-    const FusedOrders& ord = coll == kAllReduce ? c->orders : c->ring_orders;
+    const FusedOrders& ord = algo == Algo::Ring ? c->ring_orders : c->tree_orders;
     for (int r = 0; r < n; ++r) {
       // kRotate folds pointer j as the j-th rank of the shared order
       const bool rotate = ord.mode == kRotate && coll != kAllGather;
@@ -328,7 +363,7 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     a.nranks = (uint32_t)n;
     a.group = (uint32_t)p.group;
     a.height = p.height;
-    err = launch_stepwise(coll, c->algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
+    err = launch_stepwise(coll, algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
   }
   return err == hipSuccess ? EMU_SUCCESS : EMU_ERR_HIP;
 }
@@ -351,6 +386,37 @@ int emu_reduce_scatter(const void* const sendbufs[], void* const recvbufs[], siz
 int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t sendcount, int dtype,
                    void* stream) {
   return run_collective(kAllGather, sendbufs, recvbufs, sendcount, dtype, EMU_SUM, stream);
+}
+
+int emu_set_cost_model(int algo, double alpha_us, double bw_bytes_per_us) {
+  const int base = algo & 0xFF, mode = algo & ~0xFF;
+  if ((base != EMU_ALGO_RING && base != EMU_ALGO_TREE) || (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED))
+    return EMU_ERR_INVALID_ARGUMENT;
+  if (!(alpha_us >= 0.0) || !(bw_bytes_per_us > 0.0) || alpha_us > 1e9 || bw_bytes_per_us > 1e15)
+    return EMU_ERR_INVALID_ARGUMENT;
+  g_cost[mode == EMU_MODE_FUSED ? 1 : 0][base == EMU_ALGO_RING ? 0 : 1] = {alpha_us, bw_bytes_per_us};
+  return EMU_SUCCESS;
+}
+
+int emu_predict_us(int algo, size_t count, int dtype, double* us) {
+  const Comm* c = g_active;
+  if (!c) return EMU_ERR_NOT_INITIALIZED;
+  const int base = algo & 0xFF, mode = algo & ~0xFF;
+  if ((base != EMU_ALGO_RING && base != EMU_ALGO_TREE) || (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED) ||
+      !valid_dtype(dtype) || !us)
+    return EMU_ERR_INVALID_ARGUMENT;
+  *us = predict_us(*c, mode == EMU_MODE_FUSED, base == EMU_ALGO_RING ? Algo::Ring : Algo::Tree,
+                   (double)count * (double)elem_size(static_cast<DType>(dtype)));
+  return EMU_SUCCESS;
+}
+
+int emu_select_algo(size_t count, int dtype, int* algo) {
+  const Comm* c = g_active;
+  if (!c) return EMU_ERR_NOT_INITIALIZED;
+  if (!valid_dtype(dtype) || !algo) return EMU_ERR_INVALID_ARGUMENT;
+  const Algo a = c->auto_algo ? select_algo(*c, (double)count * (double)elem_size(static_cast<DType>(dtype))) : c->algo;
+  *algo = a == Algo::Ring ? EMU_ALGO_RING : EMU_ALGO_TREE;
+  return EMU_SUCCESS;
 }
 
 int emu_tree_topology(int channel, int rank, int* up, int down[3]) {

@@ -15,7 +15,7 @@ import os
 LIB_PATH = os.environ.get("EMUCOMM_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                          "libemucomm.so")
 
-ALGO = {"ring": 0, "tree": 1}
+ALGO = {"ring": 0, "tree": 1, "auto": 2}
 MODE = {"stepwise": 0x000, "fused": 0x100}
 DTYPE = {"i32": 0, "i64": 1, "f32": 2, "f16": 3, "bf16": 4}
 OP = {"sum": 0, "max": 1}
@@ -63,6 +63,12 @@ def lib() -> ctypes.CDLL:
         L.emu_tree_depth.restype = ctypes.c_int
         L.emu_comm_destroy.argtypes = []
         L.emu_comm_destroy.restype = ctypes.c_int
+        L.emu_set_cost_model.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.emu_set_cost_model.restype = ctypes.c_int
+        L.emu_predict_us.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+        L.emu_predict_us.restype = ctypes.c_int
+        L.emu_select_algo.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        L.emu_select_algo.restype = ctypes.c_int
         L.emu_strerror.argtypes = [ctypes.c_int]
         L.emu_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -145,6 +151,22 @@ def all_gather_raw(sendptrs, recvptrs, sendcount: int, dtype: int, stream: int =
 
 def all_gather(sendptrs, recvptrs, sendcount: int, dtype: str, stream: int = 0) -> None:
     _check(all_gather_raw(sendptrs, recvptrs, sendcount, DTYPE[dtype], stream), "emu_all_gather")
+
+
+def set_cost_model(algo: str, mode: str, alpha_us: float, bw_bytes_per_us: float) -> None:
+    _check(lib().emu_set_cost_model(algo_code(algo, mode), alpha_us, bw_bytes_per_us), "emu_set_cost_model")
+
+
+def predict_us(algo: str, mode: str, count: int, dtype: str) -> float:
+    out = ctypes.c_double()
+    _check(lib().emu_predict_us(algo_code(algo, mode), count, DTYPE[dtype], ctypes.byref(out)), "emu_predict_us")
+    return out.value
+
+
+def select_algo(count: int, dtype: str) -> str:
+    out = ctypes.c_int()
+    _check(lib().emu_select_algo(count, DTYPE[dtype], ctypes.byref(out)), "emu_select_algo")
+    return {v: k for k, v in ALGO.items()}[out.value]
 
 
 def tree_topology(channel: int, rank: int) -> tuple[int, list[int]]:

@@ -35,6 +35,10 @@ extern "C" {
  * emu_comm_init_graph for other chain orders and head patterns). */
 #define EMU_ALGO_RING 0
 #define EMU_ALGO_TREE 1
+/* AUTO: each all-reduce runs the ring or the tree, whichever the cost model
+ * (emu_predict_us) predicts faster for its size; reduce-scatter and
+ * all-gather always run on the ring. */
+#define EMU_ALGO_AUTO 2
 /* Execution mode, OR-ed into `algo`.
  * STEPWISE (default): every ring step / tree hop runs as a receive-reduce-
  *   copy between virtual ranks through step FIFO slots, as the pages'
@@ -89,7 +93,8 @@ extern "C" {
  * size.
  *   nranks      1..EMU_MAX_RANKS
  *   nnodes      >= 1, divides nranks
- *   algo        EMU_ALGO_RING or EMU_ALGO_TREE, optionally | EMU_MODE_FUSED
+ *   algo        EMU_ALGO_RING, EMU_ALGO_TREE or EMU_ALGO_AUTO, optionally
+ *               | EMU_MODE_FUSED
  *   nchannels   1..EMU_MAX_CHANNELS.  The message is split into nchannels
  *               disjoint ranges (page "NCCL 专家课程 13", section "前置知识");
  *               the first ceil(nchannels/2) channels use tree 0, the others
@@ -195,6 +200,37 @@ int emu_reduce_scatter(const void* const sendbufs[], void* const recvbufs[], siz
  */
 int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t sendcount, int dtype,
                    void* stream);
+
+/*
+ * Algorithm selection by a cost model: the pages' alpha-beta formulas (page
+ * "NCCL 专家课程 13", section "理想成本模型"; page "all-reduce 每张卡要发多少
+ * 数据?", section "α–β 模型") with per-(mode, algorithm) parameters.  For
+ * S = count * element size bytes per rank on the active communicator (N
+ * ranks, D the deepest channel tree):
+ *   ring: 2(N-1) * alpha + 2(N-1)/N * S / bw
+ *   tree: 2 * D * alpha  + 2 * S / bw
+ * (microseconds; the fixed cost of a call is folded into alpha).  The
+ * defaults are a least-squares fit to a message-size sweep of 8 ranks on one
+ * node measured on MI355X (per mode).  Selection takes the smaller predicted
+ * time, the ring on an exact tie (page "NCCL代码分析", section "通讯时如何选择
+ * Channel": the algorithm of least predicted time is used).
+ *
+ * emu_set_cost_model - replace alpha (us per stage, >= 0) and bw (bytes per
+ *   us, > 0) of `algo` (EMU_ALGO_RING or EMU_ALGO_TREE, optionally |
+ *   EMU_MODE_FUSED); process-wide, host only.  EMU_ERR_INVALID_ARGUMENT for
+ *   other algorithms or values out of range (state unchanged).
+ * emu_predict_us - the predicted time of one all-reduce of `count` elements of
+ *   `dtype` with `algo` (as above) on the active communicator, into *us.
+ * emu_select_algo - the algorithm an all-reduce of `count` elements of
+ *   `dtype` runs on the active communicator, into *algo (EMU_ALGO_RING or
+ *   EMU_ALGO_TREE; the fixed algorithm unless it was initialised with
+ *   EMU_ALGO_AUTO, whose choice uses the communicator's mode).
+ * Errors: EMU_ERR_NOT_INITIALIZED; EMU_ERR_INVALID_ARGUMENT for a NULL
+ * output, unknown dtype or algorithm.
+ */
+int emu_set_cost_model(int algo, double alpha_us, double bw_bytes_per_us);
+int emu_predict_us(int algo, size_t count, int dtype, double* us);
+int emu_select_algo(size_t count, int dtype, int* algo);
 
 /*
  * emu_tree_topology - the tree record of `rank` in `channel`: its parent

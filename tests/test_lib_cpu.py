@@ -35,6 +35,9 @@ def test_header_constants_match_binding():
     consts = dict(re.findall(r"#define\s+(EMU_\w+)\s+(0x[0-9A-Fa-f]+|\d+)", text))
     val = {k: int(v, 0) for k, v in consts.items()}
     assert val["EMU_ALGO_RING"] == E.ALGO["ring"] and val["EMU_ALGO_TREE"] == E.ALGO["tree"]
+    assert val["EMU_ALGO_AUTO"] == E.ALGO["auto"]
+    assert [val[f"EMU_PATTERN_{k}"] for k in ("TREE", "SPLIT_TREE", "BALANCED_TREE")] == \
+        [E.PATTERNS[k] for k in ("tree", "split", "balanced")]
     assert val["EMU_MODE_FUSED"] == E.MODE["fused"] and val["EMU_MODE_STEPWISE"] == E.MODE["stepwise"]
     for k, name in (("EMU_INT32", "i32"), ("EMU_INT64", "i64"), ("EMU_FLOAT32", "f32"),
                     ("EMU_FLOAT16", "f16"), ("EMU_BFLOAT16", "bf16")):
@@ -212,3 +215,55 @@ def test_collective_argument_errors_without_gpu():
     # absurd counts
     assert rs(send, recv, 1 << 60, 2, 0) == E.ERR_INVALID_ARGUMENT
     assert ag(send, recv, 1 << 60, 2) == E.ERR_INVALID_ARGUMENT
+
+
+DEFAULT_COST = {("stepwise", "ring"): (1.09866, 646291.0), ("stepwise", "tree"): (1.05829, 655217.0),
+                ("fused", "ring"): (0.619739, 635033.0), ("fused", "tree"): (0.596203, 748673.0)}
+
+
+def _restore_cost():
+    for (mode, algo), (a, b) in DEFAULT_COST.items():
+        E.set_cost_model(algo, mode, a, b)
+
+
+@pytest.mark.parametrize("n,m,nch", [(8, 1, 12), (16, 16, 8), (15, 15, 8), (32, 4, 16), (4, 2, 2), (64, 8, 8)])
+@pytest.mark.parametrize("mode", ["stepwise", "fused"])
+def test_cost_model_predictions_and_selection_match_the_oracle(n, m, nch, mode):
+    # Predicted times and the AUTO choice equal the oracle's formulas and
+    # selection rule (both in double precision, same operation order).
+    from oracle import costmodel as CM
+    _restore_cost()
+    try:
+        E.comm_init(n, m, "auto", nch, 1 << 19, mode=mode)
+        depth = max(ch.true_depth() for ch in T.build_topology(n, m, nch).channels)
+        for params in (None, ((2.0, 400000.0), (0.5, 90000.0))):
+            if params is not None:
+                E.set_cost_model("ring", mode, *params[0])
+                E.set_cost_model("tree", mode, *params[1])
+            ring = DEFAULT_COST[(mode, "ring")] if params is None else params[0]
+            tree = DEFAULT_COST[(mode, "tree")] if params is None else params[1]
+            for dtype, esz in (("f32", 4), ("bf16", 2), ("i64", 8)):
+                for count in [0, 1, 7, 1000, 1 << 12, 1 << 16, 123457, 1 << 20, 1 << 24, 3 << 26]:
+                    s = float(count) * esz
+                    assert E.predict_us("ring", mode, count, dtype) == CM.ring_time(n, s, *ring)
+                    assert E.predict_us("tree", mode, count, dtype) == CM.tree_time(depth, s, *tree)
+                    assert E.select_algo(count, dtype) == CM.select(n, depth, s, ring + (0.0,), tree + (0.0,))
+    finally:
+        _restore_cost()
+
+
+def test_fixed_algorithm_is_reported_and_cost_model_errors():
+    _restore_cost()
+    E.comm_init(8, 1, "tree", 12, 1 << 19)
+    assert E.select_algo(1 << 24, "f32") == "tree"
+    E.comm_init(8, 1, "ring", 12, 1 << 19, mode="fused")
+    assert E.select_algo(16, "f32") == "ring"
+    L = E.lib()
+    for bad in ((7, 1.0, 1.0), (2, 1.0, 1.0), (0, -1.0, 1.0), (0, 1.0, 0.0), (0, float("nan"), 1.0), (0x201, 1.0, 1.0)):
+        assert L.emu_set_cost_model(*bad) == E.ERR_INVALID_ARGUMENT, bad
+    import ctypes
+    out = ctypes.c_double()
+    assert L.emu_predict_us(2, 10, 2, ctypes.byref(out)) == E.ERR_INVALID_ARGUMENT    # AUTO has no formula
+    assert L.emu_predict_us(0, 10, 9, ctypes.byref(out)) == E.ERR_INVALID_ARGUMENT
+    assert L.emu_predict_us(0, 10, 2, None) == E.ERR_INVALID_ARGUMENT
+    assert L.emu_select_algo(10, 2, None) == E.ERR_INVALID_ARGUMENT

@@ -158,6 +158,12 @@ int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t 
  * EMU_ERR_INVALID_ARGUMENT; EMU_ERR_HIP when the runtime refuses an
  * allocation, copy or launch.  Faults inside kernels surface at the stream
  * synchronisation.
+ * Graph capture: the first call for a (count, dtype, op) on a device builds
+ * that shape's tables (device allocation and a synchronous copy), so it must
+ * run outside stream capture; every later call is exactly one kernel launch
+ * on `stream` (no allocation, copy or memset) and may be captured in a HIP
+ * graph and replayed.  The same holds for emu_reduce_scatter and
+ * emu_all_gather.
  */
 int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count,
                   int dtype, int op, void* stream);

@@ -25,6 +25,12 @@ hipError_t launch_stepwise(Coll coll, bool ring, DType t, Op op, const StepArgs&
                            size_t lds, hipStream_t s);
 int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds, int group);
 int stepwise_vectors_per_lane(bool ring);
+// Defined in ll.hip.
+hipError_t launch_ll(bool ring, DType t, Op op, const StepArgs& a, uint32_t* status, int grid, int block, size_t lds,
+                     hipStream_t s);
+size_t ll_lds(bool ring, int n);
+int ll_occupancy(bool ring, DType t, Op op, int block, size_t lds);
+constexpr int kLLMaxRanks = 16;   // one wave per rank in one workgroup
 
 namespace {
 
@@ -58,6 +64,7 @@ struct Plan {
   int group = 0, block = 0, grid = 0;
   size_t lds = 0;
   uint32_t height = 0;
+  bool ll = false;            // runs the LL-protocol kernels
 };
 
 struct Comm {
@@ -65,6 +72,7 @@ struct Comm {
   Algo algo = Algo::Ring;     // the fixed algorithm, or the ring for reduce-scatter / all-gather
   bool auto_algo = false;     // EMU_ALGO_AUTO: ring or tree per call, by the cost model
   bool fused = false;
+  bool ll = false;            // stepwise all-reduce with the LL protocol
   size_t chunk_bytes = 0;
   Topology topo;
   FusedOrders ring_orders;   // fused ring all-reduce and reduce-scatter: how each tile names its order
@@ -80,6 +88,21 @@ constexpr size_t kMaxCachedComms = 16;
 
 std::map<int, int> g_cu_count;
 std::map<int, size_t> g_lds_limit;
+// Per device: the word an LL kernel sets when it abandons a call.
+std::map<int, uint32_t*> g_ll_status;
+
+uint32_t* ll_status_word(int dev) {
+  auto it = g_ll_status.find(dev);
+  if (it != g_ll_status.end()) return it->second;
+  void* p = nullptr;
+  if (hipMalloc(&p, sizeof(uint32_t)) != hipSuccess) return nullptr;
+  if (hipMemset(p, 0, sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(p);
+    return nullptr;
+  }
+  g_ll_status[dev] = static_cast<uint32_t*>(p);
+  return static_cast<uint32_t*>(p);
+}
 
 size_t lds_per_block(int dev) {
   auto it = g_lds_limit.find(dev);
@@ -125,19 +148,23 @@ int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DTyp
   }
   const int n = c.nranks;
   const bool ring = algo == Algo::Ring;
-  const int vpl = stepwise_vectors_per_lane(ring);
+  // The LL protocol runs the all-reduce with one wave (64 lanes, one vector
+  // each) per rank; reduce-scatter and all-gather keep the slot protocol.
+  p->ll = c.ll && coll == kAllReduce;
+  const int vpl = p->ll ? 1 : stepwise_vectors_per_lane(ring);
   // Lanes per virtual rank: the widest group that fits one workgroup
   // (N*G <= 1024 threads) and the device's LDS per workgroup.
   const size_t lds_limit = lds_per_block(dev);
-  p->group = (int)env_long("EMU_STEP_GROUP", 64);   // tuning override; must be a power of two
+  p->group = p->ll ? 64 : (int)env_long("EMU_STEP_GROUP", 64);   // tuning override; must be a power of two
   if (p->group > 64 || (p->group & (p->group - 1))) p->group = 64;
   // LDS: ring 2 parities of slots plus 2 x N staged block descriptors and
   // 2 staged ring orders, tree 2 parities x (up, down) slots.
   auto lds_of = [&](int g) {
+    if (p->ll) return ll_lds(ring, n);
     return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes +
            (ring ? 2u * n * sizeof(RingLoopBlock) + 2u * kMaxRanks : 0u);
   };
-  while (p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
+  while (!p->ll && p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
   if (n * p->group > 1024 || lds_of(p->group) > lds_limit) return EMU_ERR_INTERNAL;
   p->block = (n * p->group + 63) / 64 * 64;
   const uint64_t slice_elems = (uint64_t)p->group * vpl * unit;
@@ -160,7 +187,8 @@ int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DTyp
   } else {
     // One pipeline per resident workgroup (tasks per CU = occupancy, or the
     // tuning override EMU_TREE_TASKS_PER_CU).
-    const int occ_t = stepwise_occupancy(false, t, op, p->block, p->lds, p->group);
+    const int occ_t = p->ll ? ll_occupancy(false, t, op, p->block, p->lds)
+                            : stepwise_occupancy(false, t, op, p->block, p->lds, p->group);
     const long per_cu = env_long("EMU_TREE_TASKS_PER_CU", occ_t);
     std::vector<TreeTask> tasks;
     std::vector<TreeNode> nodes;
@@ -172,7 +200,8 @@ int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DTyp
     if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(TreeTask))) return e;
     if (int e = p->table.upload(nodes.data(), nodes.size() * sizeof(TreeNode))) return e;
   }
-  const int occ = stepwise_occupancy(ring, t, op, p->block, p->lds, p->group);
+  const int occ = p->ll ? ll_occupancy(ring, t, op, p->block, p->lds)
+                        : stepwise_occupancy(ring, t, op, p->block, p->lds, p->group);
   p->grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntasks, (uint64_t)cus * occ));
   return EMU_SUCCESS;
 }
@@ -218,9 +247,11 @@ extern "C" {
 int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes, int pattern,
                         const int* intra) {
   const int base = algo & 0xFF;
-  const int mode = algo & ~0xFF;
+  const int mode = algo & ~0xFF & ~EMU_PROTO_LL;
+  const bool ll = (algo & EMU_PROTO_LL) != 0;
   if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE && base != EMU_ALGO_AUTO) return EMU_ERR_INVALID_ARGUMENT;
   if (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED) return EMU_ERR_INVALID_ARGUMENT;
+  if (ll && (mode == EMU_MODE_FUSED || nranks > kLLMaxRanks)) return EMU_ERR_INVALID_ARGUMENT;
   if (chunk_bytes == 0 || chunk_bytes % kVecBytes != 0 || chunk_bytes > ((size_t)1 << 30))
     return EMU_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks || nnodes < 1 || nranks % nnodes != 0 || nchannels < 1 ||
@@ -243,6 +274,7 @@ int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t 
   c->algo = base == EMU_ALGO_TREE ? Algo::Tree : Algo::Ring;
   c->auto_algo = base == EMU_ALGO_AUTO;
   c->fused = mode == EMU_MODE_FUSED;
+  c->ll = ll;
   c->chunk_bytes = chunk_bytes;
   if (int e = build_topology(nranks, nnodes, nchannels, pattern, order.data(), &c->topo)) return e;
   if (int e = build_fused_orders(c->topo, Algo::Ring, &c->ring_orders)) return e;
@@ -363,7 +395,13 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     a.nranks = (uint32_t)n;
     a.group = (uint32_t)p.group;
     a.height = p.height;
-    err = launch_stepwise(coll, algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
+    if (p.ll) {
+      uint32_t* status = ll_status_word(dev);
+      if (!status) return EMU_ERR_HIP;
+      err = launch_ll(algo == Algo::Ring, t, o, a, status, p.grid, p.block, p.lds, s);
+    } else {
+      err = launch_stepwise(coll, algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
+    }
   }
   return err == hipSuccess ? EMU_SUCCESS : EMU_ERR_HIP;
 }
@@ -439,11 +477,29 @@ int emu_tree_depth(int* depth) {
 }
 
 int emu_comm_destroy(void) {
-  bool has_plans = false;
+  bool has_plans = !g_ll_status.empty();
   for (const auto& kv : g_comms) has_plans = has_plans || !kv.second->plans.empty();
   if (has_plans) (void)hipDeviceSynchronize();
   g_active = nullptr;
   g_comms.clear();
+  for (auto& kv : g_ll_status) (void)hipFree(kv.second);
+  g_ll_status.clear();
+  return EMU_SUCCESS;
+}
+
+int emu_protocol_status(int* abandoned) {
+  if (!abandoned) return EMU_ERR_INVALID_ARGUMENT;
+  *abandoned = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
+  auto it = g_ll_status.find(dev);
+  if (it == g_ll_status.end()) return EMU_SUCCESS;
+  uint32_t v = 0;
+  if (hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
+  if (hipMemcpy(&v, it->second, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return EMU_ERR_HIP;
+  if (v && (hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
+    return EMU_ERR_HIP;
+  *abandoned = v ? 1 : 0;
   return EMU_SUCCESS;
 }
 

@@ -16,7 +16,8 @@ LIB_PATH = os.environ.get("EMUCOMM_LIB") or os.path.join(os.path.dirname(os.path
                                                          "libemucomm.so")
 
 ALGO = {"ring": 0, "tree": 1, "auto": 2}
-MODE = {"stepwise": 0x000, "fused": 0x100}
+# "ll": the stepwise mode with the LL protocol (EMU_PROTO_LL)
+MODE = {"stepwise": 0x000, "fused": 0x100, "ll": 0x200}
 DTYPE = {"i32": 0, "i64": 1, "f32": 2, "f16": 3, "bf16": 4}
 OP = {"sum": 0, "max": 1}
 ITEMSIZE = {"i32": 4, "i64": 8, "f32": 4, "f16": 2, "bf16": 2}
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.emu_predict_us.restype = ctypes.c_int
         L.emu_select_algo.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.emu_select_algo.restype = ctypes.c_int
+        L.emu_protocol_status.argtypes = [ctypes.POINTER(ctypes.c_int)]
+        L.emu_protocol_status.restype = ctypes.c_int
         L.emu_strerror.argtypes = [ctypes.c_int]
         L.emu_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -180,6 +183,14 @@ def tree_depth() -> int:
     d = ctypes.c_int(0)
     _check(lib().emu_tree_depth(ctypes.byref(d)), "emu_tree_depth")
     return d.value
+
+
+def protocol_status() -> bool:
+    """True if an LL all-reduce on the current device was abandoned since the
+    last query (waits for the device; clears the flag)."""
+    v = ctypes.c_int(0)
+    _check(lib().emu_protocol_status(ctypes.byref(v)), "emu_protocol_status")
+    return bool(v.value)
 
 
 def comm_destroy() -> None:

@@ -48,6 +48,22 @@ extern "C" {
  * Both give bit-identical results. */
 #define EMU_MODE_STEPWISE 0x000
 #define EMU_MODE_FUSED 0x100
+/* Protocol of the stepwise all-reduce, OR-ed into `algo` (page "NCCL 内部
+ * 机制：一次 AllReduce 如何变成拓扑图、Channel 与 GPU Kernel", sections
+ * "Simple：有效载荷效率与大消息吞吐" and "LL：用更高的元数据比例换低延迟").
+ * SIMPLE (default): a step's data goes through a FIFO slot and the ranks
+ *   meet at a barrier after every step.
+ * LL: every 8-byte FIFO word carries 4 data bytes and 4 flag bytes (the
+ *   item's sequence number), written and read as one access; a rank polls
+ *   the words it reads until they carry the flag it expects and publishes
+ *   how many items it consumed, so the writer knows when a slot is free.
+ *   No barriers between steps.  Stepwise mode only, at most 16 ranks (one
+ *   64-lane wave per rank); reduce-scatter and all-gather on such a
+ *   communicator run SIMPLE.  Same results, bit for bit.  Every wait is
+ *   bounded: a call whose wait expires is abandoned, its outputs are
+ *   undefined, and emu_protocol_status reports it. */
+#define EMU_PROTO_SIMPLE 0x000
+#define EMU_PROTO_LL 0x200
 
 /* Element types. */
 #define EMU_INT32 0
@@ -94,7 +110,8 @@ extern "C" {
  *   nranks      1..EMU_MAX_RANKS
  *   nnodes      >= 1, divides nranks
  *   algo        EMU_ALGO_RING, EMU_ALGO_TREE or EMU_ALGO_AUTO, optionally
- *               | EMU_MODE_FUSED
+ *               | EMU_MODE_FUSED or | EMU_PROTO_LL (not both; LL needs
+ *               nranks <= 16)
  *   nchannels   1..EMU_MAX_CHANNELS.  The message is split into nchannels
  *               disjoint ranges (page "NCCL 专家课程 13", section "前置知识");
  *               the first ceil(nchannels/2) channels use tree 0, the others
@@ -263,6 +280,18 @@ int emu_tree_depth(int* depth);
  * stream.  Destroying when nothing is initialised succeeds.
  */
 int emu_comm_destroy(void);
+
+/*
+ * emu_protocol_status - whether an LL all-reduce on the current device was
+ * abandoned (a wait expired) since the last query: *abandoned = 1 or 0.
+ * Waits for the device to go idle, then reads and clears the flag; host
+ * only, not for use under stream capture.  A correct schedule never
+ * abandons: every wait is for data or space that an earlier step of another
+ * rank provides.
+ * Errors: EMU_ERR_INVALID_ARGUMENT for NULL; EMU_ERR_HIP if the runtime
+ * fails.
+ */
+int emu_protocol_status(int* abandoned);
 
 /* emu_strerror - static description of a result code (never NULL). */
 const char* emu_strerror(int code);

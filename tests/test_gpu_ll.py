@@ -1,0 +1,158 @@
+"""Parity of the stepwise all-reduce under the LL protocol (EMU_PROTO_LL)
+with the CPU oracle, through the C ABI.
+
+The protocol changes how a step's data reaches the next rank (flag-in-line
+FIFO words polled by the reader, consumed counts published back), never
+the order of any reduction, so the bar is the same as for the slot
+protocol: bit-exact to the oracle for every type.  Every case also checks
+that no call was abandoned (emu_protocol_status)."""
+
+import numpy as np
+import pytest
+
+from double_binary_tree_amd import inputs as I
+from oracle import allreduce as A
+from tests.gpu_util import announce, run_allreduce, to_device, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from double_binary_tree_amd import emucomm as E
+    E.lib()
+    assert not E.protocol_status()
+    yield
+    E.comm_destroy()
+    torch.cuda.empty_cache()
+
+
+def _bits(x):
+    return np.ascontiguousarray(x).view(np.uint8)
+
+
+def _not_abandoned():
+    from double_binary_tree_amd import emucomm as E
+    assert not E.protocol_status(), "an LL all-reduce was abandoned"
+
+
+def _check(w, algo, count, chunk_bytes, inplace, salt=0):
+    announce(f"LL {w.name} n={w.nranks} m={w.nnodes} nch={w.nchannels} algo={algo} count={count} "
+             f"chunk={chunk_bytes} inplace={inplace}")
+    xs = I.rank_inputs(w, count=count, salt=salt)
+    want = A.allreduce(xs, w.nnodes, algo, w.nchannels, chunk_bytes, w.dtype, w.op)[0]
+    got, _ = run_allreduce(xs, w.nnodes, algo, "ll", w.nchannels, chunk_bytes, w.dtype, w.op, inplace)
+    _not_abandoned()
+    wb = _bits(want).reshape(len(want), -1)
+    for r, g in enumerate(got):
+        gb = _bits(g).reshape(len(g), -1)
+        if not np.array_equal(gb, wb):
+            first = np.nonzero((gb != wb).any(axis=1))[0]
+            raise AssertionError(f"rank {r}: {len(first)} elements differ, first at {first[:8].tolist()}")
+
+
+LL_WORKLOADS = [name for name, w in I.WORKLOADS.items() if w.nranks <= 16]
+CASES = [(name, algo) for name in LL_WORKLOADS for algo in ("ring", "tree")]
+
+
+@pytest.mark.parametrize("name,algo", CASES)
+@pytest.mark.parametrize("inplace", [False, True])
+def test_ll_small_chunks(name, algo, inplace):
+    # small chunks: many ring loops and tree chunks, several tasks per
+    # workgroup (the ring's FIFO counters run across tasks, the tree's
+    # restart at each), and a ragged tail
+    w = I.WORKLOADS[name]
+    unit = 16 // w.itemsize
+    count = 37 * 1024 + 3 * unit + (1 if unit > 1 else 0)
+    _check(w, algo, count, chunk_bytes=4096, inplace=inplace)
+
+
+@pytest.mark.parametrize("name,algo", CASES)
+def test_ll_workload_chunk(name, algo):
+    w = I.WORKLOADS[name]
+    _check(w, algo, min(w.count, 300_000 + 5), chunk_bytes=w.chunk_bytes, inplace=False, salt=1)
+
+
+EDGE_COUNTS = [1, 2, 3, 7, 8, 9, 15, 16, 17, 255, 256, 257, 1023, 1024, 1025, 4099]
+
+
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+@pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("bf16", "sum"), ("f16", "max"), ("i64", "sum")])
+def test_ll_edge_counts(algo, dtype, op):
+    w = I.Workload("edge", 7, 6, 3, (algo,), 5, 64, dtype, op, 1,
+                   ("int", -50, 50) if dtype.startswith("i") else ("normal", 1.0))
+    for count in EDGE_COUNTS:
+        _check(w, algo, count, chunk_bytes=64, inplace=(count % 2 == 1))
+
+
+@pytest.mark.parametrize("n,m,nch", [(1, 1, 1), (2, 1, 1), (2, 2, 3), (3, 3, 2), (5, 5, 7), (12, 3, 4),
+                                     (16, 16, 2), (16, 2, 5), (16, 1, 64)])
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+def test_ll_shapes(n, m, nch, algo):
+    w = I.Workload("shape", 8, n, m, (algo,), nch, 256, "f32", "sum", 1, ("normal", 1.0))
+    _check(w, algo, 6 * 1024 + 13, chunk_bytes=256, inplace=False)
+
+
+@pytest.mark.parametrize("name", ["chain8_f32", "dtree16_bf16", "dtree15_bf16"])
+def test_ll_full_size_equals_slot_protocol(name):
+    """At full size (the workload's own launch configuration): the LL result
+    equals the slot protocol's bit for bit on every element (that result is
+    held to the oracle by the full-size parity tests), every rank holds the
+    same bits, and sampled positions equal the oracle's."""
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    w = I.WORKLOADS[name]
+    xs = I.rank_inputs(w)
+    rng = np.random.default_rng(9)
+    idx = np.unique(np.concatenate([rng.integers(0, w.count, 2048), [0, w.count - 1]])).astype(np.int64)
+    sends = [to_device(x, w.dtype) for x in xs]
+    for algo in w.algos:
+        announce(f"LL full size {name} {algo}")
+        want = A.allreduce_at(xs, idx, w.nnodes, algo, w.nchannels, w.chunk_bytes, w.dtype, w.op)
+        outs = {}
+        for mode in ("stepwise", "ll"):
+            E.comm_init(w.nranks, w.nnodes, algo, w.nchannels, w.chunk_bytes, mode=mode)
+            recvs = [torch.empty_like(s) for s in sends]
+            E.allreduce_tensors(sends, recvs, w.op)
+            torch.cuda.synchronize()
+            flat = [r.view(torch.uint8) for r in recvs]
+            for r in flat[1:]:
+                assert torch.equal(r, flat[0]), f"{name} {algo} {mode}: ranks differ"
+            outs[mode] = flat[0]
+            del recvs, flat
+        _not_abandoned()
+        assert torch.equal(outs["ll"], outs["stepwise"]), f"{name} {algo}: LL differs from the slot protocol"
+        got = to_host_bits(outs["ll"].view(sends[0].dtype), w.dtype)[idx]
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"{name} {algo}: differs from the oracle"
+        del outs
+    del sends
+    torch.cuda.empty_cache()
+
+
+def test_ll_communicator_runs_reduce_scatter_and_all_gather():
+    """Reduce-scatter and all-gather on an LL communicator run the slot
+    protocol; their results are the oracle's."""
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    from oracle import collectives as C
+    w = I.Workload("coll", 8, 8, 1, ("ring",), 4, 4096, "f32", "sum", 1, ("normal", 1.0))
+    block = 4096 + 4
+    xs = I.rank_inputs(w, count=block * w.nranks)
+    E.comm_init(w.nranks, 1, "ring", w.nchannels, w.chunk_bytes, mode="ll")
+    sends = [to_device(x, "f32") for x in xs]
+    outs = [torch.empty(block, dtype=torch.float32, device="cuda") for _ in range(w.nranks)]
+    E.reduce_scatter_tensors(sends, outs, "sum")
+    torch.cuda.synchronize()
+    want = C.reduce_scatter(xs, 1, w.nchannels, w.chunk_bytes, "f32", "sum")
+    for r in range(w.nranks):
+        assert np.array_equal(to_host_bits(outs[r], "f32").view(np.uint8), want[r].view(np.uint8))
+    gathered = [torch.empty(block * w.nranks, dtype=torch.float32, device="cuda") for _ in range(w.nranks)]
+    E.all_gather_tensors(outs, gathered)
+    torch.cuda.synchronize()
+    cat = np.concatenate([to_host_bits(o, "f32") for o in outs])
+    for g in gathered:
+        assert np.array_equal(to_host_bits(g, "f32").view(np.uint8), cat.view(np.uint8))
+    _not_abandoned()

@@ -39,6 +39,7 @@ def test_header_constants_match_binding():
     assert [val[f"EMU_PATTERN_{k}"] for k in ("TREE", "SPLIT_TREE", "BALANCED_TREE")] == \
         [E.PATTERNS[k] for k in ("tree", "split", "balanced")]
     assert val["EMU_MODE_FUSED"] == E.MODE["fused"] and val["EMU_MODE_STEPWISE"] == E.MODE["stepwise"]
+    assert val["EMU_PROTO_LL"] == E.MODE["ll"] and val["EMU_PROTO_SIMPLE"] == 0
     for k, name in (("EMU_INT32", "i32"), ("EMU_INT64", "i64"), ("EMU_FLOAT32", "f32"),
                     ("EMU_FLOAT16", "f16"), ("EMU_BFLOAT16", "bf16")):
         assert val[k] == E.DTYPE[name]
@@ -137,7 +138,9 @@ def test_init_rejects_bad_arguments_and_keeps_state():
     bad = [
         (0, 1, 1, 1, 1 << 19), (65, 1, 1, 1, 1 << 19), (4, 3, 1, 1, 1 << 19), (4, 0, 1, 1, 1 << 19),
         (4, 1, 1, 0, 1 << 19), (4, 1, 1, 65, 1 << 19), (4, 1, 1, 1, 0), (4, 1, 1, 1, 24), (4, 1, 1, 1, (1 << 30) + 16),
-        (4, 1, 7, 1, 1 << 19), (4, 1, 0x201, 1, 1 << 19),
+        (4, 1, 7, 1, 1 << 19), (4, 1, 0x401, 1, 1 << 19),
+        # LL: stepwise only, at most 16 ranks
+        (4, 1, 0x301, 1, 1 << 19), (17, 1, 0x201, 1, 1 << 19), (32, 4, 0x200, 16, 1 << 19),
     ]
     for args in bad:
         assert E.comm_init_raw(*args) == E.ERR_INVALID_ARGUMENT, args
@@ -145,6 +148,14 @@ def test_init_rejects_bad_arguments_and_keeps_state():
     up, down = E.tree_topology(0, 2)
     ref = T.build_topology(4, 2, 2).channels[0]
     assert (up, down) == (ref.up[2], ref.down[2])
+
+
+def test_ll_init_accepts_up_to_16_ranks():
+    for n, m, algo in ((16, 1, "ring"), (16, 16, "tree"), (2, 2, "auto"), (1, 1, "tree")):
+        E.comm_init(n, m, algo, 4, 1 << 19, mode="ll")
+        up, down = E.tree_topology(0, n - 1)
+        ref = T.build_topology(n, m, 4).channels[0]
+        assert (up, down) == (ref.up[n - 1], ref.down[n - 1])
 
 
 def test_calls_before_init():

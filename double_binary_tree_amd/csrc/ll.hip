@@ -35,6 +35,12 @@
 
 namespace emu {
 
+// Whether a poll that failed yields the SIMD for a moment (s_sleep) before
+// the next one.
+#ifndef EMU_LL_SLEEP
+#define EMU_LL_SLEEP 1
+#endif
+
 constexpr uint32_t kLLSlots = 2;            // FIFO depth (>= 2: see the tree's stage argument)
 constexpr uint32_t kLLWords = 4;            // 8-byte words per lane per item (one 16-byte vector)
 constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait is abandoned
@@ -73,7 +79,7 @@ __device__ __forceinline__ bool ll_wait(const LLCtl& ctl, Ready ready) {
       __hip_atomic_store(ctl.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
-    __builtin_amdgcn_s_sleep(1);
+    if (EMU_LL_SLEEP) __builtin_amdgcn_s_sleep(1);
   }
 }
 

@@ -8,7 +8,8 @@ ranks on 16 nodes (the double binary tree, mirror), f32 sum, per-rank sizes
 device with a seeded generator.  Every point also checks that LL and SIMPLE
 give bit-identical results and that no LL call was abandoned.
 
-Reports per point the median per-launch time and LL / SIMPLE, and per
+Reports per point the per-launch time of back-to-back launches replayed
+from a HIP graph (so host call overhead is left out) and LL / SIMPLE, and per
 (shape, algorithm, channel count) the size intervals where each protocol
 wins, with the practical-tie rule of the course page ("NCCL 专家课程 13",
 section "性能结果的判定规则": a loser within 5% of the winner is a tie).
@@ -22,7 +23,36 @@ import argparse
 import json
 import sys
 
-from double_binary_tree_amd.sweep import CHUNK, human, intervals, time_point
+from double_binary_tree_amd.sweep import CHUNK, human, intervals
+
+GRAPH_LAUNCHES = 20
+
+
+def time_graph(E, sptr, rptr, count, torch, replays: int) -> float:
+    """Per-launch time (us) of back-to-back launches replayed from a HIP
+    graph: GRAPH_LAUNCHES all-reduces captured once (after warm calls, which
+    build the shape's tables), the graph replayed `replays` times between
+    two events.  Host-side call overhead is not in the figure."""
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        E.allreduce(sptr, rptr, count, "f32", "sum", stream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = torch.cuda.current_stream()
+        for _ in range(GRAPH_LAUNCHES):
+            E.allreduce(sptr, rptr, count, "f32", "sum", cap.cuda_stream)
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    b.record(stream)
+    b.synchronize()
+    del graph
+    return a.elapsed_time(b) * 1e3 / (replays * GRAPH_LAUNCHES)
+
 
 SHAPES = ((8, 1), (16, 16))       # (ranks, nodes)
 CHANNELS = (1, 12)
@@ -33,7 +63,6 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--max-pow", type=int, default=26, help="largest count = 2**max_pow elements")
     ap.add_argument("--min-pow", type=int, default=1)
-    ap.add_argument("--reps", type=int, default=15)
     ap.add_argument("--out", default=None, help="write a markdown report here")
     ap.add_argument("--jsonl", default=None, help="write one JSON line per point here")
     args = ap.parse_args()
@@ -52,9 +81,14 @@ def main() -> int:
     g.manual_seed(20261207)
     sends = [torch.rand(maxc, device="cuda", generator=g) * 2 - 1 for _ in range(nmax)]
     recvs = [torch.empty_like(s) for s in sends]
-    stream = torch.cuda.current_stream()
     rows = {}
     jl = open(args.jsonl, "w") if args.jsonl else None
+    # one untimed point per shape and protocol first (the first launches of a
+    # process pay one-time costs)
+    for n, m in SHAPES:
+        for proto in PROTOS:
+            E.comm_init(n, m, "ring", 1, CHUNK, mode=proto)
+            time_graph(E, [t.data_ptr() for t in sends[:n]], [t.data_ptr() for t in recvs[:n]], 2, torch, 1)
     for n, m in SHAPES:
         sptr = [t.data_ptr() for t in sends[:n]]
         rptr = [t.data_ptr() for t in recvs[:n]]
@@ -68,8 +102,8 @@ def main() -> int:
                     results = {}
                     for proto in PROTOS:
                         E.comm_init(n, m, algo, nch, CHUNK, mode=proto)
-                        reps = args.reps if count < (1 << 24) else max(5, args.reps // 3)
-                        row[proto] = time_point(E, sptr, rptr, count, stream, torch, reps)
+                        replays = 5 if count < (1 << 22) else 1
+                        row[proto] = time_graph(E, sptr, rptr, count, torch, replays)
                         results[proto] = torch.cat([r[:count] for r in recvs[:n]]).view(torch.int32).clone()
                     if not torch.equal(results["ll"], results["stepwise"]):
                         print(f"MISMATCH LL vs SIMPLE: {key} count {count}", file=sys.stderr)
@@ -92,8 +126,9 @@ def main() -> int:
 
 def write_report(path, rows):
     lines = ["# Protocol sweep: stepwise all-reduce, SIMPLE vs LL (f32 sum, one MI355X)\n\n",
-             "Command: `python -m double_binary_tree_amd.protosweep --out <this file>`. Median of per-launch "
-             "times (events on the launch stream around each launch, warm launches, buffers resident in HBM). "
+             "Command: `python -m double_binary_tree_amd.protosweep --out <this file>`. Per-launch time of "
+             f"{GRAPH_LAUNCHES} back-to-back launches captured in a HIP graph and replayed (events on the stream "
+             "around the replays; host call overhead excluded; buffers resident in HBM). "
              "SIMPLE = FIFO slot per step + workgroup barrier; LL = flag-in-line FIFO words polled by the "
              "reader, no barriers. Results bit-identical at every point.\n\n"]
     for (n, m, algo, nch), rs in rows.items():

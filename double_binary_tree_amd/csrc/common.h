@@ -76,7 +76,7 @@ struct RingTask {
   uint32_t loop;      // index into the loop table (nranks blocks per loop)
   uint32_t slice;     // slice index inside each block
   uint32_t ring;      // the loop's ring order: row of the order table
-  uint32_t pad;
+  uint32_t nslices;   // tasks of the loop (slice = 0 .. nslices - 1)
 };
 
 // Stepwise tree: one task = a run of consecutive slices of the message that

@@ -152,7 +152,8 @@ void build_ring_coll_tasks(const Topology& topo, uint64_t block, uint64_t unit, 
         loops->push_back({off, (uint32_t)piece.count, (uint32_t)(off / slice_elems)});
         nslices = std::max(nslices, ceil_div(off + piece.count, slice_elems) - off / slice_elems);
       }
-      for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q, (uint32_t)ch.ring_id, 0});
+      for (uint64_t q = 0; q < nslices; ++q)
+        tasks->push_back({loop_id, (uint32_t)q, (uint32_t)ch.ring_id, (uint32_t)nslices});
       ++loop_id;
     }
   }
@@ -356,7 +357,7 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
         if (b.count)
           nslices = std::max(nslices, ceil_div(b.offset + b.count, slice_elems) - b.offset / slice_elems);
       }
-      for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q, ring, 0});
+      for (uint64_t q = 0; q < nslices; ++q) tasks->push_back({loop_id, (uint32_t)q, ring, (uint32_t)nslices});
       ++loop_id;
     }
   }

@@ -114,7 +114,7 @@ int main(int argc, char** argv) {
                   loops[i].first_cell);
     std::printf("], \"ring_tasks\": [");
     for (size_t i = 0; i < tasks.size(); ++i)
-      std::printf("%s[%u,%u,%u]", i ? "," : "", tasks[i].loop, tasks[i].slice, tasks[i].ring);
+      std::printf("%s[%u,%u,%u,%u]", i ? "," : "", tasks[i].loop, tasks[i].slice, tasks[i].ring, tasks[i].nslices);
     std::printf("], \"ring_orders\": [");
     for (size_t i = 0; i < orders.size(); ++i) std::printf("%s%u", i ? "," : "", orders[i]);
     std::printf("],");

@@ -203,13 +203,16 @@ def test_stepwise_ring_tasks(dump, n, m, nch, chunk, esz, count, pattern, seed):
     nloops = len(blocks) // n if n else 0
     orders = d["ring_orders"]
     per_loop = {}
-    for lp, q, ring in d["ring_tasks"]:
-        per_loop.setdefault(lp, []).append(q)
+    for lp, q, ring, ns in d["ring_tasks"]:
+        per_loop.setdefault(lp, []).append((q, ns))
         # the task's ring order is its channel's
         assert orders[ring * 64: ring * 64 + n] == topo.channels[loop_chan[lp]].order
     assert sorted(per_loop) == list(range(nloops))
-    for lp, qs in per_loop.items():
+    for lp, qns in per_loop.items():
+        qs = [q for q, _ in qns]
         assert qs == list(range(len(qs)))
+        # every task carries its loop's task count (the modulus of the all-reduce's slice skew)
+        assert all(ns == len(qs) for _, ns in qns)
         for k in range(n):
             o, b, c = blocks[lp * n + k]
             covered = 0

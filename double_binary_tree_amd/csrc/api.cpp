@@ -14,6 +14,7 @@
 #include "common.h"
 #include "plan.h"
 #include "topology.h"
+#include "xwg.h"
 
 namespace emu {
 
@@ -31,6 +32,13 @@ hipError_t launch_ll(bool ring, DType t, Op op, const StepArgs& a, uint32_t* sta
 size_t ll_lds(bool ring, int n);
 int ll_occupancy(bool ring, DType t, Op op, int block, size_t lds);
 constexpr int kLLMaxRanks = 16;   // one wave per rank in one workgroup
+// Defined in xwg.hip.
+hipError_t launch_xring(bool ll, DType t, Op op, const StepArgs& a, const XArgs& x, const RingLoopBlock* loops,
+                        const uint32_t* orders, int grid, hipStream_t s);
+int xring_threads();
+int xring_slice_vectors(bool ll);
+int xring_capacity(bool ll, DType t, Op op, int cus);
+constexpr size_t kXMaxWorkspace = (size_t)4 << 30;       // per communicator and device
 
 namespace {
 
@@ -64,7 +72,19 @@ struct Plan {
   int group = 0, block = 0, grid = 0;
   size_t lds = 0;
   uint32_t height = 0;
-  bool ll = false;            // runs the LL-protocol kernels
+  bool ll = false;            // runs the LL-protocol kernels (one workgroup)
+  // stepwise ring across workgroups
+  bool xwg = false;
+  DeviceBuffer xchan, xslices;   // [nch][2] loop ranges then [nch] ring rows; [loops] slices per step
+};
+
+// FIFOs and counters of the cross-workgroup ring, per communicator and
+// device: [fifo | tail counters | head counters | abandon word], all zero
+// when created.
+struct XWorkspace {
+  DeviceBuffer mem;
+  size_t bytes = 0, fifo_bytes = 0, counter_bytes = 0;
+  uint32_t nslots = 0;
 };
 
 struct Comm {
@@ -73,7 +93,9 @@ struct Comm {
   bool auto_algo = false;     // EMU_ALGO_AUTO: ring or tree per call, by the cost model
   bool fused = false;
   bool ll = false;            // stepwise all-reduce with the LL protocol
+  bool xwg = false;           // stepwise ring all-reduce across workgroups (EMU_TRANSPORT_DEVICE)
   size_t chunk_bytes = 0;
+  std::map<int, std::unique_ptr<XWorkspace>> xws;   // device -> workspace
   Topology topo;
   FusedOrders ring_orders;   // fused ring all-reduce and reduce-scatter: how each tile names its order
   FusedOrders tree_orders;   // fused tree all-reduce (built when the tree may run)
@@ -114,6 +136,46 @@ size_t lds_per_block(int dev) {
   return (size_t)bytes;
 }
 
+// Slices per ring step that a loop can need: a block holds at most
+// chunk_bytes bytes and so spans at most chunk_bytes / slice bytes + 1 cells.
+uint64_t xring_slice_bytes(const Comm& c) { return (uint64_t)xring_slice_vectors(c.ll) * kVecBytes; }
+uint32_t xring_max_slices(const Comm& c) {
+  return (uint32_t)((c.chunk_bytes + xring_slice_bytes(c) - 1) / xring_slice_bytes(c) + 1);
+}
+
+// The communicator's workspace on `dev`, created (zeroed) on first use.
+// FIFO depth: two steps' worth of slices, so that a loop's first step can
+// start while the previous loop drains (tuning override EMU_XWG_SLOTS, at
+// least one step's worth).
+int xring_workspace(Comm& c, int dev, XWorkspace** out) {
+  auto it = c.xws.find(dev);
+  if (it != c.xws.end()) {
+    *out = it->second.get();
+    return EMU_SUCCESS;
+  }
+  const uint32_t m = xring_max_slices(c);
+  const uint64_t nslots = std::max<uint64_t>(m, (uint64_t)env_long("EMU_XWG_SLOTS", 2 * (long)m));
+  const uint64_t nfifo = (uint64_t)c.nchannels * c.nranks;
+  const uint64_t slot_bytes = (c.ll ? 2 : 1) * xring_slice_bytes(c);
+  const uint64_t fifo_bytes = nfifo * nslots * slot_bytes;
+  const uint64_t counter_bytes = nfifo * kXCounterStride * sizeof(uint32_t);
+  const uint64_t bytes = fifo_bytes + 2 * counter_bytes + 256;
+  if (nslots > UINT32_MAX || bytes > kXMaxWorkspace) return EMU_ERR_INVALID_ARGUMENT;
+  auto w = std::make_unique<XWorkspace>();
+  if (hipMalloc(&w->mem.ptr, bytes) != hipSuccess) {
+    w->mem.ptr = nullptr;
+    return EMU_ERR_HIP;
+  }
+  if (hipMemset(w->mem.ptr, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
+  w->bytes = bytes;
+  w->fifo_bytes = fifo_bytes;
+  w->counter_bytes = counter_bytes;
+  w->nslots = (uint32_t)nslots;
+  *out = w.get();
+  c.xws[dev] = std::move(w);
+  return EMU_SUCCESS;
+}
+
 int cu_count(int dev) {
   auto it = g_cu_count.find(dev);
   if (it != g_cu_count.end()) return it->second;
@@ -126,11 +188,39 @@ int cu_count(int dev) {
 
 // `count` is the elements per rank of the all-reduce, or the block size of
 // the reduce-scatter / all-gather.
-int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, Op op, Plan* p) {
+int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, Op op, Plan* p) {
   const int esz = elem_size(t);
   const uint64_t unit = kVecBytes / esz;
   const uint64_t chunk_count = c.chunk_bytes / esz;
   const int cus = cu_count(dev);
+  if (c.xwg && coll == kAllReduce) {
+    // One workgroup per (channel, ring position); all resident at once.
+    p->xwg = true;
+    const uint64_t slice_elems = (uint64_t)xring_slice_vectors(c.ll) * unit;
+    if (count / slice_elems >= ((uint64_t)1 << 32)) return EMU_ERR_INVALID_ARGUMENT;   // cell index is 32-bit
+    p->grid = c.nchannels * c.nranks;
+    if (xring_capacity(c.ll, t, op, cus) < p->grid) return EMU_ERR_INVALID_ARGUMENT;
+    XWorkspace* w = nullptr;
+    if (int e = xring_workspace(c, dev, &w)) return e;
+    std::vector<RingLoopBlock> loops;
+    std::vector<RingTask> tasks;
+    std::vector<uint32_t> orders;
+    build_ring_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks, &orders);
+    const size_t nloops = loops.size() / (size_t)c.nranks;
+    std::vector<uint32_t> slices(nloops, 0);
+    for (const RingTask& k : tasks) slices[k.loop] = k.nslices;
+    for (uint32_t m : slices)
+      if (m == 0 || m > w->nslots) return EMU_ERR_INTERNAL;
+    std::vector<uint32_t> chan = ring_channel_loops(c.topo, count, unit, chunk_count);
+    if (chan.size() != 2u * c.nchannels || (c.nchannels && chan.back() != nloops)) return EMU_ERR_INTERNAL;
+    for (const ChannelTopology& ch : c.topo.channels) chan.push_back((uint32_t)ch.ring_id);
+    if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
+    if (int e = p->orders.upload(orders.data(), orders.size() * sizeof(uint32_t))) return e;
+    if (int e = p->xchan.upload(chan.data(), chan.size() * sizeof(uint32_t))) return e;
+    if (int e = p->xslices.upload(slices.data(), slices.size() * sizeof(uint32_t))) return e;
+    p->block = xring_threads();
+    return EMU_SUCCESS;
+  }
   if (c.fused) {
     std::vector<Tile> tiles;
     const uint64_t tile_elems = (uint64_t)fused_tile_vectors() * unit;
@@ -150,7 +240,7 @@ int make_plan(const Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DTyp
   const bool ring = algo == Algo::Ring;
   // The LL protocol runs the all-reduce with one wave (64 lanes, one vector
   // each) per rank; reduce-scatter and all-gather keep the slot protocol.
-  p->ll = c.ll && coll == kAllReduce;
+  p->ll = c.ll && !c.xwg && coll == kAllReduce;
   const int vpl = p->ll ? 1 : stepwise_vectors_per_lane(ring);
   // Lanes per virtual rank: the widest group that fits one workgroup
   // (N*G <= 1024 threads) and the device's LDS per workgroup.
@@ -247,11 +337,13 @@ extern "C" {
 int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t chunk_bytes, int pattern,
                         const int* intra) {
   const int base = algo & 0xFF;
-  const int mode = algo & ~0xFF & ~EMU_PROTO_LL;
+  const int mode = algo & ~0xFF & ~EMU_PROTO_LL & ~EMU_TRANSPORT_DEVICE;
   const bool ll = (algo & EMU_PROTO_LL) != 0;
+  const bool xwg = (algo & EMU_TRANSPORT_DEVICE) != 0;
   if (base != EMU_ALGO_RING && base != EMU_ALGO_TREE && base != EMU_ALGO_AUTO) return EMU_ERR_INVALID_ARGUMENT;
   if (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED) return EMU_ERR_INVALID_ARGUMENT;
-  if (ll && (mode == EMU_MODE_FUSED || nranks > kLLMaxRanks)) return EMU_ERR_INVALID_ARGUMENT;
+  if (xwg && (mode == EMU_MODE_FUSED || base != EMU_ALGO_RING)) return EMU_ERR_INVALID_ARGUMENT;
+  if (ll && !xwg && (mode == EMU_MODE_FUSED || nranks > kLLMaxRanks)) return EMU_ERR_INVALID_ARGUMENT;
   if (chunk_bytes == 0 || chunk_bytes % kVecBytes != 0 || chunk_bytes > ((size_t)1 << 30))
     return EMU_ERR_INVALID_ARGUMENT;
   if (nranks < 1 || nranks > kMaxRanks || nnodes < 1 || nranks % nnodes != 0 || nchannels < 1 ||
@@ -275,6 +367,7 @@ int emu_comm_init_graph(int nranks, int nnodes, int algo, int nchannels, size_t 
   c->auto_algo = base == EMU_ALGO_AUTO;
   c->fused = mode == EMU_MODE_FUSED;
   c->ll = ll;
+  c->xwg = xwg;
   c->chunk_bytes = chunk_bytes;
   if (int e = build_topology(nranks, nnodes, nchannels, pattern, order.data(), &c->topo)) return e;
   if (int e = build_fused_orders(c->topo, Algo::Ring, &c->ring_orders)) return e;
@@ -395,7 +488,25 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     a.nranks = (uint32_t)n;
     a.group = (uint32_t)p.group;
     a.height = p.height;
-    if (p.ll) {
+    if (p.xwg) {
+      uint32_t* status = ll_status_word(dev);
+      if (!status) return EMU_ERR_HIP;
+      const XWorkspace& w = *c->xws.at(dev);
+      char* base = static_cast<char*>(w.mem.ptr);
+      const uint32_t* chan = static_cast<const uint32_t*>(p.xchan.ptr);
+      XArgs x{};
+      x.chan_loops = chan;
+      x.chan_ring = chan + 2 * c->nchannels;
+      x.loop_slices = static_cast<const uint32_t*>(p.xslices.ptr);
+      x.fifo = base;
+      x.tail = reinterpret_cast<uint32_t*>(base + w.fifo_bytes);
+      x.head = reinterpret_cast<uint32_t*>(base + w.fifo_bytes + w.counter_bytes);
+      x.abandon = reinterpret_cast<uint32_t*>(base + w.fifo_bytes + 2 * w.counter_bytes);
+      x.status = status;
+      x.nslots = w.nslots;
+      err = launch_xring(c->ll, t, o, a, x, static_cast<const RingLoopBlock*>(p.table.ptr),
+                         static_cast<const uint32_t*>(p.orders.ptr), p.grid, s);
+    } else if (p.ll) {
       uint32_t* status = ll_status_word(dev);
       if (!status) return EMU_ERR_HIP;
       err = launch_ll(algo == Algo::Ring, t, o, a, status, p.grid, p.block, p.lds, s);
@@ -508,8 +619,17 @@ int emu_protocol_status(int* abandoned) {
   uint32_t v = 0;
   if (hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
   if (hipMemcpy(&v, it->second, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return EMU_ERR_HIP;
-  if (v && (hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
-    return EMU_ERR_HIP;
+  if (v) {
+    // An abandoned cross-workgroup call leaves its FIFO counters mismatched:
+    // clear every such workspace on the device with the status word.
+    if (hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess) return EMU_ERR_HIP;
+    for (const auto& kv : g_comms) {
+      auto w = kv.second->xws.find(dev);
+      if (w != kv.second->xws.end() && hipMemset(w->second->mem.ptr, 0, w->second->bytes) != hipSuccess)
+        return EMU_ERR_HIP;
+    }
+    if (hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
+  }
   *abandoned = v ? 1 : 0;
   return EMU_SUCCESS;
 }

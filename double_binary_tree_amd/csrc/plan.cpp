@@ -363,6 +363,19 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
   }
 }
 
+std::vector<uint32_t> ring_channel_loops(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count) {
+  std::vector<uint32_t> out;
+  uint32_t first = 0;
+  const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
+  for (int c = 0; c < topo.nchannels; ++c) {
+    const uint32_t nloops = (uint32_t)ring_loops(chans[c], topo.nranks, chunk_count, unit).size();
+    out.push_back(first);
+    out.push_back(first + nloops);
+    first += nloops;
+  }
+  return out;
+}
+
 void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t slice_elems,
                       uint64_t target_tasks, std::vector<TreeTask>* tasks,
                       std::vector<TreeNode>* nodes) {

@@ -69,6 +69,10 @@ void build_ring_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
                       uint64_t slice_elems, std::vector<RingLoopBlock>* loops,
                       std::vector<RingTask>* tasks, std::vector<uint32_t>* orders);
 
+// Stepwise ring across workgroups: per channel, the range [first, end) of
+// its loops in build_ring_tasks' loop table ([nch][2]).
+std::vector<uint32_t> ring_channel_loops(const Topology& topo, uint64_t count, uint64_t unit, uint64_t chunk_count);
+
 // Stepwise tree: about target_tasks contiguous pieces of the message, each
 // inside one run of channels with the same tree records and cut at
 // slice-cell boundaries, and the per-(channel, rank) tree table.

@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("EMUCOMM_LIB") or os.path.join(os.path.dirname(os.path
 
 ALGO = {"ring": 0, "tree": 1, "auto": 2}
 # "ll": the stepwise mode with the LL protocol (EMU_PROTO_LL)
-MODE = {"stepwise": 0x000, "fused": 0x100, "ll": 0x200}
+MODE = {"stepwise": 0x000, "fused": 0x100, "ll": 0x200, "xwg": 0x400, "xwg_ll": 0x600}
 DTYPE = {"i32": 0, "i64": 1, "f32": 2, "f16": 3, "bf16": 4}
 OP = {"sum": 0, "max": 1}
 ITEMSIZE = {"i32": 4, "i64": 8, "f32": 4, "f16": 2, "bf16": 2}

@@ -64,6 +64,26 @@ extern "C" {
  *   undefined, and emu_protocol_status reports it. */
 #define EMU_PROTO_SIMPLE 0x000
 #define EMU_PROTO_LL 0x200
+/* Transport of the stepwise ring all-reduce, OR-ed into `algo` (page "NCCL
+ * 内部机制：…", sections "Chunk、slice、step 是三个尺度" and "Ring：带宽友
+ * 好…": one CTA per channel on every GPU, steps handed over through FIFO
+ * buffers).  DEVICE: every (channel, ring position) is a workgroup of its
+ * own, all resident at once (a cooperative launch), and a step's data
+ * travels through FIFOs in device memory, nslots 4 KiB slices deep, made
+ * visible across the chip's L2 caches: with EMU_PROTO_SIMPLE by a release
+ * fence plus a tail counter, with EMU_PROTO_LL by flag-in-line 8-byte words
+ * (any nranks).  Ring only (EMU_ALGO_RING, stepwise); reduce-scatter and
+ * all-gather on such a communicator run the one-workgroup stepwise kernels.
+ * Same results, bit for bit.  The FIFOs and counters (per communicator and
+ * device, nchannels * nranks FIFOs of twice the slices a chunk spans, 8 KiB
+ * a slice with LL, 4 KiB without; at most 4 GiB) are created on the first
+ * all-reduce and reused: calls of one communicator must not overlap (order
+ * them on one stream).  The first call fails with EMU_ERR_INVALID_ARGUMENT
+ * when nchannels * nranks workgroups cannot be resident at once or the
+ * FIFOs would exceed 4 GiB.  Every wait is bounded; an abandoned call
+ * leaves its outputs undefined, later calls do nothing until
+ * emu_protocol_status has reported it (and cleared the FIFOs). */
+#define EMU_TRANSPORT_DEVICE 0x400
 
 /* Element types. */
 #define EMU_INT32 0
@@ -111,7 +131,8 @@ extern "C" {
  *   nnodes      >= 1, divides nranks
  *   algo        EMU_ALGO_RING, EMU_ALGO_TREE or EMU_ALGO_AUTO, optionally
  *               | EMU_MODE_FUSED or | EMU_PROTO_LL (not both; LL needs
- *               nranks <= 16)
+ *               nranks <= 16), or EMU_ALGO_RING | EMU_TRANSPORT_DEVICE,
+ *               optionally | EMU_PROTO_LL (any nranks)
  *   nchannels   1..EMU_MAX_CHANNELS.  The message is split into nchannels
  *               disjoint ranges (page "NCCL 专家课程 13", section "前置知识");
  *               the first ceil(nchannels/2) channels use tree 0, the others
@@ -282,10 +303,11 @@ int emu_tree_depth(int* depth);
 int emu_comm_destroy(void);
 
 /*
- * emu_protocol_status - whether an LL all-reduce on the current device was
- * abandoned (a wait expired) since the last query: *abandoned = 1 or 0.
- * Waits for the device to go idle, then reads and clears the flag; host
- * only, not for use under stream capture.  A correct schedule never
+ * emu_protocol_status - whether an LL or EMU_TRANSPORT_DEVICE all-reduce on
+ * the current device was abandoned (a wait expired) since the last query:
+ * *abandoned = 1 or 0.  Waits for the device to go idle, then reads and
+ * clears the flag (and, if it was set, every EMU_TRANSPORT_DEVICE FIFO
+ * workspace on the device); host only, not for use under stream capture.  A correct schedule never
  * abandons: every wait is for data or space that an earlier step of another
  * rank provides.
  * Errors: EMU_ERR_INVALID_ARGUMENT for NULL; EMU_ERR_HIP if the runtime

@@ -40,6 +40,7 @@ def test_header_constants_match_binding():
         [E.PATTERNS[k] for k in ("tree", "split", "balanced")]
     assert val["EMU_MODE_FUSED"] == E.MODE["fused"] and val["EMU_MODE_STEPWISE"] == E.MODE["stepwise"]
     assert val["EMU_PROTO_LL"] == E.MODE["ll"] and val["EMU_PROTO_SIMPLE"] == 0
+    assert val["EMU_TRANSPORT_DEVICE"] == E.MODE["xwg"] and E.MODE["xwg_ll"] == E.MODE["xwg"] | E.MODE["ll"]
     for k, name in (("EMU_INT32", "i32"), ("EMU_INT64", "i64"), ("EMU_FLOAT32", "f32"),
                     ("EMU_FLOAT16", "f16"), ("EMU_BFLOAT16", "bf16")):
         assert val[k] == E.DTYPE[name]
@@ -141,6 +142,9 @@ def test_init_rejects_bad_arguments_and_keeps_state():
         (4, 1, 7, 1, 1 << 19), (4, 1, 0x401, 1, 1 << 19),
         # LL: stepwise only, at most 16 ranks
         (4, 1, 0x301, 1, 1 << 19), (17, 1, 0x201, 1, 1 << 19), (32, 4, 0x200, 16, 1 << 19),
+        # device transport: stepwise ring only; unknown flag bits
+        (4, 1, 0x401, 1, 1 << 19), (4, 1, 0x402, 1, 1 << 19), (4, 1, 0x500, 1, 1 << 19),
+        (4, 1, 0x601, 1, 1 << 19), (4, 1, 0x700, 1, 1 << 19), (4, 1, 0x800, 1, 1 << 19),
     ]
     for args in bad:
         assert E.comm_init_raw(*args) == E.ERR_INVALID_ARGUMENT, args
@@ -153,6 +157,15 @@ def test_init_rejects_bad_arguments_and_keeps_state():
 def test_ll_init_accepts_up_to_16_ranks():
     for n, m, algo in ((16, 1, "ring"), (16, 16, "tree"), (2, 2, "auto"), (1, 1, "tree")):
         E.comm_init(n, m, algo, 4, 1 << 19, mode="ll")
+        up, down = E.tree_topology(0, n - 1)
+        ref = T.build_topology(n, m, 4).channels[0]
+        assert (up, down) == (ref.up[n - 1], ref.down[n - 1])
+
+
+def test_device_transport_init_accepts_ring_with_any_rank_count():
+    # the LL protocol over device FIFOs has no 16-rank limit
+    for n, m, mode in ((64, 8, "xwg"), (64, 8, "xwg_ll"), (1, 1, "xwg"), (17, 1, "xwg_ll")):
+        E.comm_init(n, m, "ring", 4, 1 << 19, mode=mode)
         up, down = E.tree_topology(0, n - 1)
         ref = T.build_topology(n, m, 4).channels[0]
         assert (up, down) == (ref.up[n - 1], ref.down[n - 1])

@@ -120,6 +120,77 @@ def rank_inputs(w: Workload, count: int | None = None, salt: int = 0) -> list[np
     return [draw(np.random.Generator(np.random.PCG64(ch)), w.dtype, w.dist, n) for ch in children]
 
 
+# Float layouts: (storage bits, exponent bits, significand bits).
+_FLOAT_BITS = {"f32": (32, 8, 23), "f16": (16, 5, 10), "bf16": (16, 8, 7)}
+
+SPECIAL_TINY, SPECIAL_MIXED, SPECIAL_HUGE, SPECIAL_INF = 0, 1, 2, 3
+
+
+def special_inputs(nranks: int, dtype: str, count: int, seed: int):
+    """Inputs made of IEEE special values, built bit by bit (float types only).
+
+    Every position gets a class and a sign, shared by all ranks:
+      SPECIAL_TINY   every rank holds a subnormal or a zero of random sign,
+                     with a significand below 2**(m-6) (m significand bits),
+                     so any sum of up to 64 of them stays subnormal and exact;
+      SPECIAL_MIXED  each rank holds a zero, a subnormal (any significand) or
+                     a normal number of magnitude about 1, of random sign;
+      SPECIAL_HUGE   two distinct ranks hold numbers of the largest finite
+                     binade with the position's sign, the others mixed
+                     values (one rank: mixed);
+      SPECIAL_INF    one rank holds infinity with the position's sign, every
+                     other rank infinity of that sign with probability 1/5,
+                     else a mixed value.
+    No NaN, and no position holds infinities or largest-binade numbers of
+    both signs, so no sum can produce a NaN.
+
+    Returns (inputs, cls, sign): one array per rank in the storage type
+    (bf16 as uint16 bits), and the per-position class and sign (1 = negative).
+    """
+    width, ebits, mbits = _FLOAT_BITS[dtype]
+    utype = np.uint32 if width == 32 else np.uint16
+    emax = (1 << ebits) - 1                 # all-ones exponent: infinity
+    bias = (1 << (ebits - 1)) - 1
+    children = np.random.SeedSequence(SEED_BASE + 7000 + seed).spawn(nranks + 1)
+    shared = np.random.Generator(np.random.PCG64(children[-1]))
+    cls = shared.integers(0, 4, size=count)
+    if nranks == 1:
+        cls = np.where(cls == SPECIAL_HUGE, SPECIAL_MIXED, cls)
+    sign = shared.integers(0, 2, size=count)
+    first = shared.integers(0, nranks, size=count)
+    second = (first + 1 + shared.integers(0, max(nranks - 1, 1), size=count)) % nranks
+
+    def pack(sg, ex, mant):
+        return ((sg.astype(np.uint64) << (width - 1)) | (ex.astype(np.uint64) << mbits) |
+                mant.astype(np.uint64)).astype(utype)
+
+    out = []
+    for r in range(nranks):
+        rng = np.random.Generator(np.random.PCG64(children[r]))
+        rsign = rng.integers(0, 2, size=count)
+        mant = rng.integers(0, 1 << mbits, size=count)
+        kind = rng.integers(0, 3, size=count)          # mixed: 0 zero, 1 subnormal, 2 normal
+        ex = np.where(kind == 2, bias + rng.integers(-4, 5, size=count), 0)
+        mant = np.where(kind == 0, 0, mant)
+        bits = pack(rsign, ex, mant)
+        tiny = pack(rsign, np.zeros(count, dtype=np.int64), rng.integers(0, 1 << (mbits - 6) if mbits > 6 else 2,
+                                                                         size=count))
+        huge = pack(sign, np.full(count, emax - 1), rng.integers(0, 1 << mbits, size=count))
+        inf = pack(sign, np.full(count, emax), np.zeros(count, dtype=np.int64))
+        bits = np.where(cls == SPECIAL_TINY, tiny, bits)
+        is_huge = (cls == SPECIAL_HUGE) & ((first == r) | (second == r))
+        bits = np.where(is_huge, huge, bits)
+        is_inf = (cls == SPECIAL_INF) & ((first == r) | (rng.random(count) < 0.2))
+        bits = np.where(is_inf, inf, bits)
+        if dtype == "f32":
+            out.append(bits.view(np.float32))
+        elif dtype == "f16":
+            out.append(bits.view(np.float16))
+        else:
+            out.append(bits)
+    return out, cls, sign
+
+
 def intra_orders(nranks: int, nnodes: int, nchannels: int, seed: int, distinct: int = 3) -> list[list[int]]:
     """Seeded per-channel rank orders for graph test cases: each channel takes
     one of ``distinct`` random orders, each a permutation of every node's

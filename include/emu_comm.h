@@ -94,8 +94,10 @@ extern "C" {
 
 /* Reduction operators.  Sum: integers wrap; floats are rounded to the
  * buffer type after every hop (f16/bf16: exact f32 add, then round to
- * nearest even).  Max: float max orders -0 below +0, so its result does not
- * depend on the order. */
+ * nearest even), subnormals kept, overflow gives infinity.  Max: float max
+ * orders -0 below +0, so its result does not depend on the order.  Float
+ * inputs must not hold NaN (a NaN result, or a NaN input to max, is outside
+ * the contract: its bits are unspecified). */
 #define EMU_SUM 0
 #define EMU_MAX 1
 

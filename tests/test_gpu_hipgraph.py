@@ -30,15 +30,20 @@ def _bits(x):
     return np.ascontiguousarray(x).view(np.uint8)
 
 
-@pytest.mark.parametrize("name,algo", [("chain8_f32", "ring"), ("dtree16_bf16", "tree"), ("hier4x8_f16", "tree"),
-                                       ("chain8_f32", "tree")])
-@pytest.mark.parametrize("mode", ["fused", "stepwise", "ll"])
+# every mode where it applies: LL in LDS up to 16 ranks, the device-memory
+# transport on the ring only
+CAPTURE_CASES = [(name, algo, mode)
+                 for name, algo in [("chain8_f32", "ring"), ("dtree16_bf16", "tree"), ("hier4x8_f16", "tree"),
+                                    ("chain8_f32", "tree")]
+                 for mode in ["fused", "stepwise", "ll", "xwg", "xwg_ll"]
+                 if not (mode == "ll" and I.WORKLOADS[name].nranks > 16) and not (mode.startswith("xwg") and algo != "ring")]
+
+
+@pytest.mark.parametrize("name,algo,mode", CAPTURE_CASES)
 def test_captured_allreduce_replays(name, algo, mode):
     import torch
     from double_binary_tree_amd import emucomm as E
     w = I.WORKLOADS[name]
-    if mode == "ll" and w.nranks > 16:
-        pytest.skip("LL needs at most 16 ranks")
     count = 50_003
     E.comm_init(w.nranks, w.nnodes, algo, w.nchannels, 8192, mode=mode)
     xs = I.rank_inputs(w, count=count)
@@ -61,7 +66,7 @@ def test_captured_allreduce_replays(name, algo, mode):
         want = A.allreduce(ys, w.nnodes, algo, w.nchannels, 8192, w.dtype, w.op)[0]
         for r in recvs:
             assert np.array_equal(_bits(to_host_bits(r, w.dtype)), _bits(want)), f"replay {rep}"
-    if mode == "ll":
+    if mode in ("ll", "xwg", "xwg_ll"):
         assert not E.protocol_status()
 
 

@@ -5,7 +5,9 @@
 //   i32/i64 sum : two's-complement wrap
 //   f32 sum     : one IEEE add, round to nearest even, subnormals kept
 //   f16 sum     : the correctly rounded f16 add (native packed f16 add)
-//   bf16 sum    : exact f32 add, then round to nearest even into bf16
+//   bf16 sum    : f32 add, then round to nearest even into bf16 (the
+//                 hardware conversion); equal to the correctly rounded bf16
+//                 add, since f32 carries more than 2p+2 significand bits
 //   max         : integers plain; floats in "key" space, where the bit
 //                 pattern is mapped to a signed integer that orders -0
 //                 below +0 and otherwise follows the float order, so the
@@ -28,21 +30,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef long long i64x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 template <typename T, typename U>
 __device__ __forceinline__ T bits(U v) {
   return __builtin_bit_cast(T, v);
-}
-
-// bf16 rounding of the f32 values held in u (one per 32-bit lane): round to
-// nearest even on the upper 16 bits; NaN keeps its upper half with the quiet
-// bit set.  Result in the low 16 bits of each lane.
-__device__ __forceinline__ u32x4 bf16_round_lo(u32x4 u) {
-  const u32x4 rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  const u32x4 quiet = (u >> 16) | 0x40u;
-  const i32x4 is_nan = (u & 0x7FFFFFFFu) > 0x7F800000u;   // -1 where NaN
-  const u32x4 m = bits<u32x4>(is_nan);
-  return (quiet & m) | (rounded & ~m);
 }
 
 template <DType T, Op O>
@@ -112,11 +105,12 @@ template <>
 struct Red<DType::BF16, Op::Sum> {
   static __device__ __forceinline__ u32x4 pre(u32x4 x) { return x; }
   static __device__ __forceinline__ u32x4 post(u32x4 x) { return x; }
+  // Widen both operands to f32 (exact), add, and round the sums to bf16
+  // with the hardware's round-to-nearest-even conversion (subnormals kept
+  // under the kernel's float mode; overflow gives infinity).
   static __device__ __forceinline__ u32x4 op(u32x4 a, u32x4 b) {
-    // element 0 of each 32-bit lane sits in the low half, element 1 in the high half
-    const f32x4 lo = bits<f32x4>(a << 16) + bits<f32x4>(b << 16);
-    const f32x4 hi = bits<f32x4>(a & 0xFFFF0000u) + bits<f32x4>(b & 0xFFFF0000u);
-    return bf16_round_lo(bits<u32x4>(lo)) | (bf16_round_lo(bits<u32x4>(hi)) << 16);
+    const f32x8 s = __builtin_convertvector(bits<bf16x8>(a), f32x8) + __builtin_convertvector(bits<bf16x8>(b), f32x8);
+    return bits<u32x4>(__builtin_convertvector(s, bf16x8));
   }
 };
 // 16-bit float key, same idea as the f32 key, on each half.

@@ -69,7 +69,7 @@ __device__ __forceinline__ void step_barrier() {
 #define EMU_TREE_VPT 1
 #endif
 #ifndef EMU_TREE_PREFETCH
-#define EMU_TREE_PREFETCH 1
+#define EMU_TREE_PREFETCH 2
 #endif
 #ifndef EMU_TREE_PREFETCH_WAVE
 #define EMU_TREE_PREFETCH_WAVE 3
@@ -381,19 +381,18 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
     const int dn_lag = H + depth;        // broadcast slice q at stage q + dn_lag
     const int nstages = nslices + 2 * H;
 
-    // The own input of reduce slice q is loaded PF stages ahead into queue
-    // entry q mod PF.  The stage loop is unrolled by PF with a per-wave
-    // phase (stage st0 + i reduces a slice = i mod PF), and every entry is
-    // refilled unconditionally (a load of nothing when there is no slice),
-    // so entries rotate by name and are never merged or copied while their
-    // loads are in flight.  Stages before 0 only refill; every wave still
-    // meets the barriers of stages 0 .. nstages-1 in order.  Without WAVE a
-    // wave may hold several ranks with different lags, so the queue is one
-    // entry deep and the phase is 0 for all.
-    static_assert(WAVE || kPrefetch == 1, "a multi-rank wave needs a one-entry queue");
-    const int ph = ((up_lag % kPrefetch) + kPrefetch) % kPrefetch;
+    // The own input that a rank reduces at stage st is loaded PF stages
+    // earlier into queue entry st mod PF: the stage loop is unrolled by PF,
+    // and at unrolled position i every lane loads the slice it will reduce
+    // PF stages later into entry i and reduces the one in entry i.  The
+    // entry depends on the stage only, not on the rank's lag, so a wave that
+    // holds ranks of different depths (G < 64) uses the same queue.  Every
+    // entry is refilled unconditionally (a load of nothing when there is no
+    // slice), so entries rotate by name and are never merged or copied while
+    // their loads are in flight.  Stages -PF .. -1 only refill; every wave
+    // meets the barriers of stages 0 .. nstages-1 in order.
     u32x4 q[kPrefetch][V];
-    for (int st0 = ph - kPrefetch; st0 < nstages; st0 += kPrefetch) {
+    for (int st0 = -kPrefetch; st0 < nstages; st0 += kPrefetch) {
 #pragma unroll
       for (int i = 0; i < kPrefetch; ++i) {
         const int st = st0 + i;

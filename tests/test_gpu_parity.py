@@ -126,8 +126,9 @@ def test_deterministic_and_modes_agree(algo, mode):
         assert np.array_equal(_bits(x), _bits(z))
 
 
-@pytest.mark.parametrize("mode", ["fused", "stepwise", "ll"])
-@pytest.mark.parametrize("name", ["hier4x8_f16", "dtree16_bf16"])
+@pytest.mark.parametrize("name,mode", [("hier4x8_f16", "fused"), ("hier4x8_f16", "stepwise"),
+                                       ("dtree16_bf16", "fused"), ("dtree16_bf16", "stepwise"),
+                                       ("dtree16_bf16", "ll")])   # LL in LDS: at most 16 ranks
 def test_parity_in_library_layout(name, mode):
     """Buffers placed by emu_buffer_layout (one pool, staggered slots):
     the same bits as the oracle."""
@@ -135,8 +136,6 @@ def test_parity_in_library_layout(name, mode):
     from double_binary_tree_amd import emucomm as E
     from tests.gpu_util import to_device, to_host_bits
     w = I.WORKLOADS[name]
-    if mode == "ll" and w.nranks > 16:
-        pytest.skip("LL needs at most 16 ranks")
     count = 200_003
     announce(f"library layout {name} {mode} count={count}")
     xs = I.rank_inputs(w, count=count, salt=3)

@@ -67,6 +67,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_capi_check() -> str:
+    """The C program that exercises the ABI from plain C (tests/host/capi_check.c),
+    built as a shared library that the GPU tests load in-process; it links
+    libemucomm.so from the package directory."""
+    src = os.path.join(ROOT, "tests", "host", "capi_check.c")
+    out = os.path.join(ROOT, "tests", "host", "libcapi_check.so")
+    cc = shutil.which("gcc") or "gcc"
+    tmp = out + ".tmp"
+    _run([cc, "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
+          f"-I{ROCM}/include", f"-I{os.path.join(ROOT, 'include')}", src, "-o", tmp,
+          f"-L{PKG}", "-lemucomm", "-Wl,-rpath,$ORIGIN/../../double_binary_tree_amd", f"-L{ROCM}/lib", "-lamdhip64",
+          f"-Wl,-rpath,{ROCM}/lib"])
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     path = build(verbose="-v" in sys.argv)
     print(path)

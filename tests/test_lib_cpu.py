@@ -312,3 +312,12 @@ def test_fixed_algorithm_is_reported_and_cost_model_errors():
     assert L.emu_predict_us(0, 10, 9, ctypes.byref(out)) == E.ERR_INVALID_ARGUMENT
     assert L.emu_predict_us(0, 10, 2, None) == E.ERR_INVALID_ARGUMENT
     assert L.emu_select_algo(10, 2, None) == E.ERR_INVALID_ARGUMENT
+
+
+def test_c_abi_check_library_is_built():
+    """The plain-C ABI check (run on the GPU by tests/test_gpu_capi.py) is
+    built and links the library; nothing is called here."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "host", "libcapi_check.so")
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "capi_check")

@@ -504,6 +504,9 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
       x.abandon = reinterpret_cast<uint32_t*>(base + w.fifo_bytes + 2 * w.counter_bytes);
       x.status = status;
       x.nslots = w.nslots;
+      // polls before a wait is abandoned; EMU_XWG_SPIN_LIMIT lowers it so
+      // that tests can force the abandon path from the host
+      x.spin_limit = (uint32_t)env_long("EMU_XWG_SPIN_LIMIT", 1L << 22);
       err = launch_xring(c->ll, t, o, a, x, static_cast<const RingLoopBlock*>(p.table.ptr),
                          static_cast<const uint32_t*>(p.orders.ptr), p.grid, s);
     } else if (p.ll) {

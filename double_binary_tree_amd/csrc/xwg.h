@@ -22,6 +22,7 @@ struct XArgs {
   uint32_t* abandon;            // nonzero once a call was abandoned (sticky until the host resets it)
   uint32_t* status;             // set when a call is abandoned
   uint32_t nslots;              // FIFO depth in slices, at least every loop's loop_slices
+  uint32_t spin_limit;          // polls before a wait is abandoned
 };
 
 }  // namespace emu

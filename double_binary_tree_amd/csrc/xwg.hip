@@ -44,7 +44,7 @@
 // Every workgroup of a call must be resident at once (a wait can be for
 // any other workgroup), so the call is a cooperative launch, which the
 // runtime refuses when the grid does not fit.  Every wait is bounded
-// (kXSpinLimit polls); on expiry the workgroup sets the abandon word and
+// (x.spin_limit polls); on expiry the workgroup sets the abandon word and
 // the status word.  Every other wait gives up once it sees the abandon word,
 // and a call that starts with it set does nothing: after an abandoned call
 // the FIFO counters no longer match, so the host must clear the workspace
@@ -64,7 +64,6 @@ constexpr int kXThreads = 256;
 #define EMU_XWG_VPT_LL 2
 #endif
 constexpr int kXVSimple = EMU_XWG_VPT_SIMPLE, kXVLL = EMU_XWG_VPT_LL;
-constexpr uint32_t kXSpinLimit = 1u << 22;    // polls before a wait is abandoned
 constexpr uint32_t kXWords = 4;               // LL: 8-byte words per 16-byte vector
 // s_waitcnt operand: vector memory count 0, the export and LDS/scalar counts
 // left at their maxima (no wait on them)
@@ -137,7 +136,7 @@ __global__ __launch_bounds__(kXThreads) void xring(const StepArgs a, const XArgs
           wg_seen = v;
           break;
         }
-        if (it >= kXSpinLimit || ((it & 63) == 63 && xload_relaxed(x.abandon))) {
+        if (it >= x.spin_limit || ((it & 63) == 63 && xload_relaxed(x.abandon))) {
           give_up();
           wg_bad = 1;
           break;
@@ -202,7 +201,7 @@ __global__ __launch_bounds__(kXThreads) void xring(const StepArgs a, const XArgs
             ready = ready && (uint32_t)(wd[j][q] >> 32) == flag;
           }
         if (ready) break;
-        if (it >= kXSpinLimit || ((it & 63) == 63 && xload_relaxed(x.abandon))) {
+        if (it >= x.spin_limit || ((it & 63) == 63 && xload_relaxed(x.abandon))) {
           give_up();
           good = false;
           break;

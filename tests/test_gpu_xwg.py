@@ -191,3 +191,49 @@ def test_xwg_communicator_runs_reduce_scatter_and_all_gather(mode):
     for g in gathered:
         assert np.array_equal(to_host_bits(g, "f32").view(np.uint8), cat.view(np.uint8))
     _not_abandoned()
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_xwg_abandoned_call_is_reported_and_recovered(mode, monkeypatch):
+    """Failure handling, forced from the host: EMU_XWG_SPIN_LIMIT=1 makes
+    every wait give up after two polls, so the call abandons (every
+    workgroup still exits).  Until emu_protocol_status has reported it, a
+    later call does nothing (the abandon word is sticky, the FIFO counters
+    no longer match); the report clears the FIFOs, and the next call is
+    correct again."""
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    w = I.Workload("abandon", 9, 8, 1, ("ring",), 4, 4096, "f32", "sum", 1, ("normal", 1.0))
+    count = 1 << 20
+    xs = I.rank_inputs(w, count=count, salt=5)
+    want = A.allreduce(xs, 1, "ring", w.nchannels, w.chunk_bytes, "f32", "sum")[0]
+    E.comm_init(w.nranks, 1, "ring", w.nchannels, w.chunk_bytes, mode=mode)
+    sends = [to_device(x, "f32") for x in xs]
+    recvs = [torch.empty_like(s) for s in sends]
+    assert not E.protocol_status()
+    abandoned = False
+    for attempt in range(5):
+        announce(f"{mode} forced abandon, attempt {attempt}")
+        monkeypatch.setenv("EMU_XWG_SPIN_LIMIT", "1")
+        E.allreduce_tensors(sends, recvs, "sum")
+        monkeypatch.delenv("EMU_XWG_SPIN_LIMIT")
+        torch.cuda.synchronize()
+        for r in recvs:
+            r.fill_(-7.0)
+        E.allreduce_tensors(sends, recvs, "sum")      # normal limit
+        torch.cuda.synchronize()
+        if E.protocol_status():
+            # the second call found the abandon word set and left the outputs alone
+            for r in recvs:
+                assert bool((r == -7.0).all()), "a call after an abandoned one wrote its outputs"
+            abandoned = True
+            break
+        # neither call abandoned: both completed, and the outputs are right
+        assert np.array_equal(to_host_bits(recvs[0], "f32").view(np.uint8), want.view(np.uint8))
+    assert abandoned, "a spin limit of 1 never made a wait give up"
+    assert not E.protocol_status()
+    E.allreduce_tensors(sends, recvs, "sum")
+    torch.cuda.synchronize()
+    assert not E.protocol_status()
+    for r in recvs:
+        assert np.array_equal(to_host_bits(r, "f32").view(np.uint8), want.view(np.uint8))

@@ -27,8 +27,8 @@ hipError_t launch_stepwise(Coll coll, bool ring, DType t, Op op, const StepArgs&
 int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds, int group);
 int stepwise_vectors_per_lane(bool ring);
 // Defined in ll.hip.
-hipError_t launch_ll(bool ring, DType t, Op op, const StepArgs& a, uint32_t* status, int grid, int block, size_t lds,
-                     hipStream_t s);
+hipError_t launch_ll(bool ring, DType t, Op op, const StepArgs& a, uint32_t* status, uint32_t spin_limit, int grid,
+                     int block, size_t lds, hipStream_t s);
 size_t ll_lds(bool ring, int n);
 int ll_occupancy(bool ring, DType t, Op op, int block, size_t lds);
 constexpr int kLLMaxRanks = 16;   // one wave per rank in one workgroup
@@ -512,7 +512,10 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     } else if (p.ll) {
       uint32_t* status = ll_status_word(dev);
       if (!status) return EMU_ERR_HIP;
-      err = launch_ll(algo == Algo::Ring, t, o, a, status, p.grid, p.block, p.lds, s);
+      // polls before a wait is abandoned; EMU_LL_SPIN_LIMIT lowers it so
+      // that tests can force the abandon path from the host
+      const uint32_t spin = (uint32_t)env_long("EMU_LL_SPIN_LIMIT", 1L << 22);
+      err = launch_ll(algo == Algo::Ring, t, o, a, status, spin, p.grid, p.block, p.lds, s);
     } else {
       err = launch_stepwise(coll, algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
     }

@@ -21,8 +21,11 @@
 // the lines it reads and the slots it writes.  Every rank runs its steps in
 // the order of the stepwise schedule and every wait is for an item produced
 // (or consumed) at an earlier step of that schedule, so the waits cannot
-// form a cycle; every wait is nevertheless bounded (kSpinLimit polls), and
-// on expiry the workgroup abandons the call and records it in *status.
+// form a cycle; every wait is nevertheless bounded (spin_limit polls, 2^22
+// unless the host lowers it), and on expiry the workgroup abandons the call
+// and records it in *status.  A wave that abandons stops working but still
+// meets every workgroup barrier (the tree's task boundaries), so the
+// workgroup always ends together.
 //
 // The pages split a tree CTA's threads 70/30 between reduce and broadcast
 // for LL (section "runTreeSplit 如何流水").  A rank here is one wave, whose
@@ -43,7 +46,6 @@ namespace emu {
 
 constexpr uint32_t kLLSlots = 2;            // FIFO depth (>= 2: see the tree's stage argument)
 constexpr uint32_t kLLWords = 4;            // 8-byte words per lane per item (one 16-byte vector)
-constexpr uint32_t kSpinLimit = 1u << 22;   // polls before a wait is abandoned
 constexpr uint32_t kG = 64;                 // lanes per rank
 
 // One rank's FIFO in LDS: [kLLSlots][kLLWords][kG] words.
@@ -64,8 +66,9 @@ __device__ __forceinline__ void lds_release32(uint32_t* p, uint32_t v) {
 
 // Per-workgroup protocol state in LDS after the FIFOs: the abandon flag.
 struct LLCtl {
-  uint32_t* abandon;   // set once any wave's wait expired
-  uint32_t* status;    // device word the host reads (emu_protocol_status)
+  uint32_t* abandon;     // set once any wave's wait expired
+  uint32_t* status;      // device word the host reads (emu_protocol_status)
+  uint32_t spin_limit;   // polls before a wait is abandoned
 };
 
 // Poll until every lane's `ready()` holds.  Returns false if the wait
@@ -74,7 +77,7 @@ template <typename Ready>
 __device__ __forceinline__ bool ll_wait(const LLCtl& ctl, Ready ready) {
   for (uint32_t it = 0;; ++it) {
     if (__all(ready())) return true;
-    if (it >= kSpinLimit || lds_acquire32(ctl.abandon)) {
+    if (it >= ctl.spin_limit || lds_acquire32(ctl.abandon)) {
       lds_release32(ctl.abandon, 1u);
       __hip_atomic_store(ctl.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
@@ -133,7 +136,8 @@ __device__ __forceinline__ bool ll_recv(const LLCtl& ctl, const uint64_t* fifo, 
 template <typename R, int ESZ>
 __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask* __restrict__ tasks,
                                                  const RingLoopBlock* __restrict__ loops,
-                                                 const uint32_t* __restrict__ orders, uint32_t* status) {
+                                                 const uint32_t* __restrict__ orders, uint32_t* status,
+                                                 uint32_t spin_limit) {
   constexpr int unit = kVecBytes / ESZ;
   extern __shared__ uint64_t lds_words[];   // fifo [N][kFifoWords], consumed [N], abandon
   const uint32_t n = a.nranks;
@@ -142,7 +146,7 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
   const uint32_t prev = (r + n - 1) % n;
   uint64_t* const fifo = lds_words;
   uint32_t* const consumed = reinterpret_cast<uint32_t*>(lds_words + (size_t)n * kFifoWords);
-  const LLCtl ctl{consumed + n, status};
+  const LLCtl ctl{consumed + n, status, spin_limit};
   for (uint32_t e = threadIdx.x; e < n * kFifoWords; e += blockDim.x) fifo[e] = 0;
   if (threadIdx.x <= n) consumed[threadIdx.x] = 0;   // and the abandon flag
   __syncthreads();
@@ -217,7 +221,8 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
 // (between two workgroup barriers).
 template <typename R, int ESZ>
 __global__ __launch_bounds__(1024) void ll_tree(const StepArgs a, const TreeTask* __restrict__ tasks,
-                                                 const TreeNode* __restrict__ nodes, uint32_t* status) {
+                                                 const TreeNode* __restrict__ nodes, uint32_t* status,
+                                                 uint32_t spin_limit) {
   constexpr int unit = kVecBytes / ESZ;
   // LDS: up FIFOs [N][kFifoWords], down FIFOs [N][kFifoWords], consumed-up
   // [N], consumed-down [N][3], abandon
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(1024) void ll_tree(const StepArgs a, const TreeTask
   uint64_t* const dn_fifo = lds_words + (size_t)n * kFifoWords;
   uint32_t* const up_used = reinterpret_cast<uint32_t*>(lds_words + 2 * (size_t)n * kFifoWords);
   uint32_t* const dn_used = up_used + n;   // [N][3]: child slot j of rank i reads down[i]
-  const LLCtl ctl{dn_used + 3 * n, status};
+  const LLCtl ctl{dn_used + 3 * n, status, spin_limit};
   if (threadIdx.x == 0) *ctl.abandon = 0;
   const int H = (int)a.height;
   const uint32_t slice_elems = kG * unit;
@@ -298,7 +303,8 @@ __global__ __launch_bounds__(1024) void ll_tree(const StepArgs a, const TreeTask
     const int nstages = nslices + 2 * H;
     u32x4 own = {0, 0, 0, 0};   // the next reduce slice's own input, once loaded
     bool have_own = false;
-    for (int st = 0; st < nstages; ++st) {
+    bool ok = true;   // false once a wait of this wave gave up: the wave then only meets the barriers
+    for (int st = 0; st < nstages && ok; ++st) {
       const int qu = st - up_lag;
       if (qu >= 0 && qu < nslices) {
         u32x4 acc = have_own ? own : load(qu);
@@ -308,27 +314,40 @@ __global__ __launch_bounds__(1024) void ll_tree(const StepArgs a, const TreeTask
           const int c = down[j];
           if (c < 0) continue;
           u32x4 y;
-          if (!ll_recv(ctl, up_fifo + (size_t)c * kFifoWords, &up_used[c], nrecv_up[j]++, p, y)) return;
+          if (!ll_recv(ctl, up_fifo + (size_t)c * kFifoWords, &up_used[c], nrecv_up[j]++, p, y)) {
+            ok = false;
+            break;
+          }
           acc = R::op(acc, y);
         }
+        if (!ok) break;
         if (qu + 1 < nslices) {   // the next reduce slice's own input, read during the waits ahead
           own = load(qu + 1);
           have_own = true;
         }
         if (is_root) {
           store(qu, acc);
-          if (has_children && !send_down(acc)) return;
+          if (has_children && !send_down(acc)) {
+            ok = false;
+            break;
+          }
         } else if (!ll_send(ctl, up_fifo + (size_t)r * kFifoWords, &up_used[r], nup++, p, acc)) {
-          return;
+          ok = false;
+          break;
         }
       }
       const int qd = st - dn_lag;
       if (!is_root && qd >= 0 && qd < nslices) {
         u32x4 x;
-        if (!ll_recv(ctl, dn_fifo + (size_t)up * kFifoWords, &dn_used[3 * up + my_slot], nrecv_dn++, p, x))
-          return;
+        if (!ll_recv(ctl, dn_fifo + (size_t)up * kFifoWords, &dn_used[3 * up + my_slot], nrecv_dn++, p, x)) {
+          ok = false;
+          break;
+        }
         store(qd, x);
-        if (has_children && !send_down(x)) return;
+        if (has_children && !send_down(x)) {
+          ok = false;
+          break;
+        }
       }
     }
     __syncthreads();   // every FIFO item of the task consumed before the restart
@@ -346,34 +365,35 @@ static hipError_t ll_allow_lds(K kernel, size_t lds) {
 }
 
 template <DType T, Op O>
-static hipError_t launch_ll_t(bool ring, const StepArgs& a, uint32_t* status, int grid, int block, size_t lds,
-                              hipStream_t s) {
+static hipError_t launch_ll_t(bool ring, const StepArgs& a, uint32_t* status, uint32_t spin_limit, int grid,
+                              int block, size_t lds, hipStream_t s) {
   if (ring) {
     if (hipError_t e = ll_allow_lds(ll_ring<Red<T, O>, Unit<T>::esz>, lds)) return e;
     hipLaunchKernelGGL((ll_ring<Red<T, O>, Unit<T>::esz>), dim3(grid), dim3(block), lds, s, a,
                        static_cast<const RingTask*>(a.tasks), static_cast<const RingLoopBlock*>(a.table), a.orders,
-                       status);
+                       status, spin_limit);
   } else {
     if (hipError_t e = ll_allow_lds(ll_tree<Red<T, O>, Unit<T>::esz>, lds)) return e;
     hipLaunchKernelGGL((ll_tree<Red<T, O>, Unit<T>::esz>), dim3(grid), dim3(block), lds, s, a,
-                       static_cast<const TreeTask*>(a.tasks), static_cast<const TreeNode*>(a.table), status);
+                       static_cast<const TreeTask*>(a.tasks), static_cast<const TreeNode*>(a.table), status,
+                       spin_limit);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ll(bool ring, DType t, Op op, const StepArgs& a, uint32_t* status, int grid, int block, size_t lds,
-                     hipStream_t s) {
+hipError_t launch_ll(bool ring, DType t, Op op, const StepArgs& a, uint32_t* status, uint32_t spin_limit, int grid,
+                     int block, size_t lds, hipStream_t s) {
   switch (t) {
-    case DType::I32: return op == Op::Sum ? launch_ll_t<DType::I32, Op::Sum>(ring, a, status, grid, block, lds, s)
-                                          : launch_ll_t<DType::I32, Op::Max>(ring, a, status, grid, block, lds, s);
-    case DType::I64: return op == Op::Sum ? launch_ll_t<DType::I64, Op::Sum>(ring, a, status, grid, block, lds, s)
-                                          : launch_ll_t<DType::I64, Op::Max>(ring, a, status, grid, block, lds, s);
-    case DType::F32: return op == Op::Sum ? launch_ll_t<DType::F32, Op::Sum>(ring, a, status, grid, block, lds, s)
-                                          : launch_ll_t<DType::F32, Op::Max>(ring, a, status, grid, block, lds, s);
-    case DType::F16: return op == Op::Sum ? launch_ll_t<DType::F16, Op::Sum>(ring, a, status, grid, block, lds, s)
-                                          : launch_ll_t<DType::F16, Op::Max>(ring, a, status, grid, block, lds, s);
-    case DType::BF16: return op == Op::Sum ? launch_ll_t<DType::BF16, Op::Sum>(ring, a, status, grid, block, lds, s)
-                                           : launch_ll_t<DType::BF16, Op::Max>(ring, a, status, grid, block, lds, s);
+    case DType::I32: return op == Op::Sum ? launch_ll_t<DType::I32, Op::Sum>(ring, a, status, spin_limit, grid, block, lds, s)
+                                          : launch_ll_t<DType::I32, Op::Max>(ring, a, status, spin_limit, grid, block, lds, s);
+    case DType::I64: return op == Op::Sum ? launch_ll_t<DType::I64, Op::Sum>(ring, a, status, spin_limit, grid, block, lds, s)
+                                          : launch_ll_t<DType::I64, Op::Max>(ring, a, status, spin_limit, grid, block, lds, s);
+    case DType::F32: return op == Op::Sum ? launch_ll_t<DType::F32, Op::Sum>(ring, a, status, spin_limit, grid, block, lds, s)
+                                          : launch_ll_t<DType::F32, Op::Max>(ring, a, status, spin_limit, grid, block, lds, s);
+    case DType::F16: return op == Op::Sum ? launch_ll_t<DType::F16, Op::Sum>(ring, a, status, spin_limit, grid, block, lds, s)
+                                          : launch_ll_t<DType::F16, Op::Max>(ring, a, status, spin_limit, grid, block, lds, s);
+    case DType::BF16: return op == Op::Sum ? launch_ll_t<DType::BF16, Op::Sum>(ring, a, status, spin_limit, grid, block, lds, s)
+                                           : launch_ll_t<DType::BF16, Op::Max>(ring, a, status, spin_limit, grid, block, lds, s);
   }
   return hipErrorInvalidValue;
 }

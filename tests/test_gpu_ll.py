@@ -156,3 +156,39 @@ def test_ll_communicator_runs_reduce_scatter_and_all_gather():
     for g in gathered:
         assert np.array_equal(to_host_bits(g, "f32").view(np.uint8), cat.view(np.uint8))
     _not_abandoned()
+
+
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+def test_ll_abandoned_call_is_reported_and_the_next_call_is_right(algo, monkeypatch):
+    """Failure handling, forced from the host: EMU_LL_SPIN_LIMIT=1 makes
+    every wait give up after two polls, so the call abandons; every wave
+    still meets the workgroup barriers and the kernel ends.  The status word
+    reports it, and the next call (normal limit; the FIFOs live in LDS and
+    restart with every launch) is bit-exact again."""
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    w = I.Workload("abandon", 9, 8, 2, (algo,), 4, 4096, "f32", "sum", 1, ("normal", 1.0))
+    count = 1 << 20
+    xs = I.rank_inputs(w, count=count, salt=6)
+    want = A.allreduce(xs, w.nnodes, algo, w.nchannels, w.chunk_bytes, "f32", "sum")[0]
+    E.comm_init(w.nranks, w.nnodes, algo, w.nchannels, w.chunk_bytes, mode="ll")
+    sends = [to_device(x, "f32") for x in xs]
+    recvs = [torch.empty_like(s) for s in sends]
+    assert not E.protocol_status()
+    abandoned = False
+    for attempt in range(5):
+        announce(f"LL {algo} forced abandon, attempt {attempt}")
+        monkeypatch.setenv("EMU_LL_SPIN_LIMIT", "1")
+        E.allreduce_tensors(sends, recvs, "sum")
+        monkeypatch.delenv("EMU_LL_SPIN_LIMIT")
+        torch.cuda.synchronize()
+        if E.protocol_status():
+            abandoned = True
+            break
+    assert abandoned, "a spin limit of 1 never made a wait give up"
+    assert not E.protocol_status()
+    E.allreduce_tensors(sends, recvs, "sum")
+    torch.cuda.synchronize()
+    assert not E.protocol_status()
+    for r in recvs:
+        assert np.array_equal(to_host_bits(r, "f32").view(np.uint8), want.view(np.uint8))

@@ -73,5 +73,41 @@ def test_full_size_sampled(name):
         for key, o in outs.items():
             assert torch.equal(o, ref), f"{name} {algo} {key} differs from fused out-of-place"
         del outs
-    del sends
+    del sends, xs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("nch", [1, 32])
+def test_sweep_largest_message_sampled(nch):
+    """The largest point of the ring/tree size sweep (8 ranks, 256 MiB of f32
+    per rank) at the smallest and largest channel count of the sweep, ring
+    and tree, fused and stepwise: sampled positions (and every channel, loop
+    and rank-chunk edge) equal the oracle's, all ranks hold the same bits,
+    and the modes agree on every byte."""
+    import torch
+    from dataclasses import replace
+    from double_binary_tree_amd import emucomm as E
+    w = replace(I.WORKLOADS["sweep8_f32"], nchannels=nch, count=1 << 26)
+    announce(f"sweep maximum: 8 ranks x 256 MiB f32, {nch} channels")
+    xs = I.rank_inputs(w)
+    idx = _sample(w, w.count, np.random.default_rng(6))
+    sends = [to_device(x, w.dtype) for x in xs]
+    for algo in ("ring", "tree"):
+        outs = {}
+        for mode in ("fused", "stepwise"):
+            announce(f"  sweep maximum {nch} ch {algo} {mode}")
+            E.comm_init(w.nranks, w.nnodes, algo, nch, w.chunk_bytes, mode=mode)
+            recvs = [torch.empty_like(s) for s in sends]
+            E.allreduce_tensors(sends, recvs, w.op)
+            torch.cuda.synchronize()
+            for r in recvs[1:]:
+                assert torch.equal(r, recvs[0]), f"{algo} {mode}: ranks differ"
+            outs[mode] = recvs[0]
+            del recvs
+        assert torch.equal(outs["fused"], outs["stepwise"]), f"{algo}: fused and stepwise differ"
+        got = to_host_bits(outs["fused"], w.dtype)[idx]
+        del outs
+        want = A.allreduce_at(xs, idx, w.nnodes, algo, nch, w.chunk_bytes, w.dtype, w.op)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"{algo}: sampled outputs differ"
+    del sends, xs
     torch.cuda.empty_cache()

@@ -127,10 +127,16 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
   // name as the tree does, were each about 15% slower here.)
   RingLoopBlock* desc = reinterpret_cast<RingLoopBlock*>(fifo + 2 * (size_t)n * V * g);   // [2][N]
   uint8_t* order = reinterpret_cast<uint8_t*>(desc + 2 * n);                                // [2][kMaxRanks]
+  // The staged descriptor of block b holds, in place of the block's first
+  // cell, the cell this task reads and writes in it (its slice q of the
+  // block, skewed per block for the all-reduce), so the steps compute no
+  // index modulo the slice count.
   auto stage_desc = [&](uint32_t t, uint32_t set) {
     if (t < a.ntasks && threadIdx.x < n) {
       const RingTask tk = tasks[t];
-      desc[set * n + threadIdx.x] = loops[(size_t)tk.loop * n + threadIdx.x];
+      RingLoopBlock d = loops[(size_t)tk.loop * n + threadIdx.x];
+      d.first_cell += kSkew ? (tk.slice + threadIdx.x * kSkew) % tk.nslices : tk.slice;
+      desc[set * n + threadIdx.x] = d;
       order[set * kMaxRanks + threadIdx.x] = (uint8_t)orders[(size_t)tk.ring * kMaxRanks + threadIdx.x];
     }
   };
@@ -139,7 +145,6 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
 
   uint32_t set = 0;
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x, set ^= 1) {
-    const RingTask task = tasks[t];
     const RingLoopBlock* blk = desc + set * n;
     // the rank at position r
     const uint32_t me = active ? wave_u32<WAVE>(order[set * kMaxRanks + r]) : 0;
@@ -158,9 +163,8 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     auto view_of = [&](uint32_t b) -> View {
       const RingLoopBlock d = blk[b];
       const uint64_t start = wave_u64<WAVE>(d.offset);
-      const uint32_t nelem = wave_u32<WAVE>(d.nelem), first = wave_u32<WAVE>(d.first_cell);
-      const uint32_t q = kSkew ? (task.slice + b * kSkew) % task.nslices : task.slice;
-      return {((uint64_t)first + q) * slice_elems, start, start + nelem};
+      const uint32_t nelem = wave_u32<WAVE>(d.nelem), cell = wave_u32<WAVE>(d.first_cell);
+      return {(uint64_t)cell * slice_elems, start, start + nelem};
     };
     auto nbytes_of = [&](const View& w, uint64_t pos) -> int {
       if (pos < w.start || pos >= w.end) return 0;
@@ -251,8 +255,11 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
       for (int v = 0; v < V; ++v) slot(0, r, v) = R::pre(own[v]);
     }
     step_barrier();
+    // block of step s, (r - s) mod N, and of step s + PF, counted down step by step
+    uint32_t b = r, bpf = (r + 2 * n - kPrefetch) % n;
     for (uint32_t s = 1; s < n; ++s) {
-      const uint32_t b = (r + n - s) % n;
+      b = b == 0 ? n - 1 : b - 1;
+      bpf = bpf == 0 ? n - 1 : bpf - 1;
       if (active) {
         u32x4 mine[V];
 #pragma unroll
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
         for (int i = 0; i + 1 < kPrefetch; ++i)
 #pragma unroll
           for (int v = 0; v < V; ++v) q[i][v] = q[i + 1][v];
-        if (s + kPrefetch < n) load_block((r + 2 * n - s - kPrefetch) % n, q[kPrefetch - 1], true);
+        if (s + kPrefetch < n) load_block(bpf, q[kPrefetch - 1], true);
         fix_block(b, mine);
         u32x4 res[V];
 #pragma unroll
@@ -274,9 +281,11 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     }
     }
     if (COLL == kReduceScatter) continue;
-    // all-gather steps 1..N-1
+    // all-gather steps 1..N-1: block (r + 1 - j) mod N, counted down
+    uint32_t bg = (r + 1) % n;
     for (uint32_t j = 1; j < n; ++j) {
-      const uint32_t b = (r + 1 + n - j) % n;
+      bg = bg == 0 ? n - 1 : bg - 1;
+      const uint32_t b = bg;
       if (active) {
         u32x4 x[V];
 #pragma unroll

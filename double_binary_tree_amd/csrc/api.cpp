@@ -305,8 +305,8 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
 // message-size sweep of 8 ranks on one node measured on MI355X.
 struct Cost { double alpha_us, bw; };
 Cost g_cost[2][2] = {          // [stepwise, fused][ring, tree]
-    {{1.17936, 670714.0}, {1.0679, 724566.0}},
-    {{0.627038, 674078.0}, {0.60984, 793955.0}},
+    {{1.10419, 625415.0}, {1.09448, 659195.0}},
+    {{0.672418, 631521.0}, {0.632165, 737631.0}},
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

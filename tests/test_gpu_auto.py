@@ -13,8 +13,8 @@ from tests.gpu_util import announce, run_allreduce
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = {("stepwise", "ring"): (1.17936, 670714.0), ("stepwise", "tree"): (1.0679, 724566.0),
-            ("fused", "ring"): (0.627038, 674078.0), ("fused", "tree"): (0.60984, 793955.0)}
+DEFAULTS = {("stepwise", "ring"): (1.10419, 625415.0), ("stepwise", "tree"): (1.09448, 659195.0),
+            ("fused", "ring"): (0.672418, 631521.0), ("fused", "tree"): (0.632165, 737631.0)}
 
 
 @pytest.fixture(scope="module", autouse=True)

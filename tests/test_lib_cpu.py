@@ -262,8 +262,8 @@ def test_collective_argument_errors_without_gpu():
     assert ag(send, recv, 1 << 60, 2) == E.ERR_INVALID_ARGUMENT
 
 
-DEFAULT_COST = {("stepwise", "ring"): (1.17936, 670714.0), ("stepwise", "tree"): (1.0679, 724566.0),
-                ("fused", "ring"): (0.627038, 674078.0), ("fused", "tree"): (0.60984, 793955.0)}
+DEFAULT_COST = {("stepwise", "ring"): (1.10419, 625415.0), ("stepwise", "tree"): (1.09448, 659195.0),
+                ("fused", "ring"): (0.672418, 631521.0), ("fused", "tree"): (0.632165, 737631.0)}
 
 
 def _restore_cost():

@@ -189,20 +189,26 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
       continue;
     }
     if (!send(R::pre(own))) return;
-    own = load((r + n - 1) % n);   // step 1's own input, read while waiting
+    // blocks counted down instead of taken modulo N: step s works on block
+    // (r - s) mod N, all-gather step j on (r + 1 - j) mod N
+    uint32_t b = r == 0 ? n - 1 : r - 1;
+    own = load(b);   // step 1's own input, read while waiting
     for (uint32_t s = 1; s < n; ++s) {
-      const uint32_t b = (r + n - s) % n;
       u32x4 y;
       if (!recv(y)) return;
       const u32x4 res = R::op(R::pre(own), y);
-      if (s + 1 < n) own = load((r + n - s - 1) % n);
+      const uint32_t bn = b == 0 ? n - 1 : b - 1;   // block of step s + 1
+      if (s + 1 < n) own = load(bn);
       if (s == n - 1) store(b, res);
       if (!send(res)) return;
+      b = bn;
     }
+    uint32_t bg = r;
     for (uint32_t j = 1; j < n; ++j) {
       u32x4 x;
       if (!recv(x)) return;
-      store((r + 1 + n - j) % n, x);
+      store(bg, x);
+      bg = bg == 0 ? n - 1 : bg - 1;
       if (j + 1 < n && !send(x)) return;
     }
   }

@@ -238,9 +238,13 @@ __global__ __launch_bounds__(kXThreads) void xring(const StepArgs a, const XArgs
   const uint32_t loop_begin = x.chan_loops[2 * c], loop_end = x.chan_loops[2 * c + 1];
   for (uint32_t l = loop_begin; l < loop_end; ++l) {
     const uint32_t m = x.loop_slices[l];
+    // block of step s: reduce-scatter (r - s) mod N, all-gather (r + 1 - j)
+    // mod N with j = s - N + 1; counted down step by step (the first
+    // all-gather step works on block r)
+    uint32_t b = r;
     for (uint32_t s = 0; s + 1 < 2 * n; ++s) {
-      // block of step s: reduce-scatter r - s, all-gather r + 1 - j (j = s - n + 1)
-      const uint32_t b = s < n ? (r + n - s) % n : (r + 1 + n - (s - n + 1)) % n;
+      if (s == n) b = r;
+      else if (s > 0) b = b == 0 ? n - 1 : b - 1;
       const RingLoopBlock d = loops[(size_t)l * n + b];
       const uint64_t end = d.offset + d.nelem;
       for (uint32_t q = 0; q < m; ++q) {

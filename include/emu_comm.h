@@ -69,14 +69,15 @@ extern "C" {
  * 好…": one CTA per channel on every GPU, steps handed over through FIFO
  * buffers).  DEVICE: every (channel, ring position) is a workgroup of its
  * own, all resident at once (a cooperative launch), and a step's data
- * travels through FIFOs in device memory, nslots 4 KiB slices deep, made
+ * travels through FIFOs in device memory, slice by slice, made
  * visible across the chip's L2 caches: with EMU_PROTO_SIMPLE by a release
  * fence plus a tail counter, with EMU_PROTO_LL by flag-in-line 8-byte words
  * (any nranks).  Ring only (EMU_ALGO_RING, stepwise); reduce-scatter and
  * all-gather on such a communicator run the one-workgroup stepwise kernels.
  * Same results, bit for bit.  The FIFOs and counters (per communicator and
- * device, nchannels * nranks FIFOs of twice the slices a chunk spans, 8 KiB
- * a slice with LL, 4 KiB without; at most 4 GiB) are created on the first
+ * device, nchannels * nranks FIFOs of twice the slices a chunk spans; a
+ * slice is 32 KiB with SIMPLE, 8 KiB of data in 16 KiB of flagged words with
+ * LL; at most 4 GiB) are created on the first
  * all-reduce and reused: calls of one communicator must not overlap (order
  * them on one stream).  The first call fails with EMU_ERR_INVALID_ARGUMENT
  * when nchannels * nranks workgroups cannot be resident at once or the

@@ -153,3 +153,36 @@ def test_parity_in_library_layout(name, mode):
     if mode == "ll":
         assert not E.protocol_status()
     del pool, sends, recvs
+
+
+@pytest.mark.parametrize("mode", ["fused", "stepwise", "ll"])
+def test_two_streams_at_once(mode):
+    """Calls of one communicator on two streams, enqueued back to back
+    without a wait between them (the fused, stepwise and LL kernels keep no
+    state on the device between calls: their tables are read-only), each on
+    its own buffers: both results are the oracle's."""
+    import torch
+    from double_binary_tree_amd import emucomm as E
+    from tests.gpu_util import to_device, to_host_bits
+    w = I.Workload("streams", 9, 8, 2, ("tree",), 6, 8192, "f32", "sum", 1, ("normal", 1.0))
+    count = 300_007
+    E.comm_init(w.nranks, w.nnodes, "tree", w.nchannels, w.chunk_bytes, mode=mode)
+    sets = []
+    for salt in (21, 22):
+        xs = I.rank_inputs(w, count=count, salt=salt)
+        sends = [to_device(x, "f32") for x in xs]
+        recvs = [torch.empty_like(s) for s in sends]
+        sets.append((xs, sends, recvs))
+    E.allreduce_tensors(sets[0][1], sets[0][2], "sum")   # builds the plan outside the concurrent part
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    for st, (_, sends, recvs) in zip(streams, sets):
+        E.allreduce([s.data_ptr() for s in sends], [r.data_ptr() for r in recvs], count, "f32", "sum",
+                    st.cuda_stream)
+    torch.cuda.synchronize()
+    if mode == "ll":
+        assert not E.protocol_status()
+    for xs, _, recvs in sets:
+        want = A.allreduce(xs, w.nnodes, "tree", w.nchannels, w.chunk_bytes, "f32", "sum")[0]
+        for r in recvs:
+            assert np.array_equal(_bits(to_host_bits(r, "f32")), _bits(want))

@@ -64,6 +64,7 @@ struct FusedArgs {
   uint64_t block_bytes;       // reduce-scatter / all-gather: bytes per block
   uint32_t ntiles;
   uint32_t nranks;
+  uint32_t xcd_runs;          // nonzero: each XCD takes a contiguous run of tiles
 };
 
 // Stepwise ring: one task = slice q of every rank-chunk of one ring loop.

@@ -32,6 +32,7 @@ constexpr int kFusedThreads = EMU_FUSED_THREADS;
 #define EMU_FUSED_BATCH 8
 #endif
 constexpr int kVpt = EMU_FUSED_VPT;      // vectors per lane in a full tile
+constexpr uint32_t kXcds = 8;            // accelerator complex dies of the chip
 constexpr int kBatch = EMU_FUSED_BATCH;  // ranks whose loads are issued back to back
 static_assert(kBatch >= 4, "the remainder of a batch is folded 4, 2 and 1 inputs at a time");
 
@@ -218,7 +219,12 @@ __global__ __launch_bounds__(kFusedThreads) void fused_collective(const FusedArg
                                                                   const uint32_t* __restrict__ rows) {
   constexpr uint32_t unit = kVecBytes / ESZ;
   constexpr uint32_t stride = kFusedThreads * kVecBytes;   // bytes between a lane's vectors
-  for (uint32_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+  // Workgroups are dealt to the chip's 8 XCDs in turn.  With xcd_runs each
+  // XCD takes a contiguous run of tiles instead of every eighth one, so the
+  // workgroups running at once spread over 8 distant parts of the buffers.
+  uint32_t vb = blockIdx.x;
+  if (a.xcd_runs && gridDim.x % kXcds == 0) vb = (blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+  for (uint32_t t = vb; t < a.ntiles; t += gridDim.x) {
     const Tile tile = tiles[t];
     const uint64_t base = tile.start * ESZ;
     const uint32_t lane_off = threadIdx.x * kVecBytes;

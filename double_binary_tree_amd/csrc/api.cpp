@@ -50,6 +50,15 @@ long env_long(const char* name, long fallback) {
   return (end && *end == '\0' && x > 0) ? x : fallback;
 }
 
+// As env_long, but 0 is a valid value.
+long env_count(const char* name, long fallback) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return fallback;
+  char* end = nullptr;
+  const long x = std::strtol(v, &end, 10);
+  return (end && *end == '\0' && x >= 0) ? x : fallback;
+}
+
 struct DeviceBuffer {
   void* ptr = nullptr;
   ~DeviceBuffer() { if (ptr) (void)hipFree(ptr); }
@@ -512,7 +521,7 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
       x.nslots = w.nslots;
       // polls before a wait is abandoned; EMU_XWG_SPIN_LIMIT lowers it so
       // that tests can force the abandon path from the host
-      x.spin_limit = (uint32_t)env_long("EMU_XWG_SPIN_LIMIT", 1L << 22);
+      x.spin_limit = (uint32_t)env_count("EMU_XWG_SPIN_LIMIT", 1L << 22);
       err = launch_xring(c->ll, t, o, a, x, static_cast<const RingLoopBlock*>(p.table.ptr),
                          static_cast<const uint32_t*>(p.orders.ptr), p.grid, s);
     } else if (p.ll) {
@@ -520,7 +529,7 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
       if (!status) return EMU_ERR_HIP;
       // polls before a wait is abandoned; EMU_LL_SPIN_LIMIT lowers it so
       // that tests can force the abandon path from the host
-      const uint32_t spin = (uint32_t)env_long("EMU_LL_SPIN_LIMIT", 1L << 22);
+      const uint32_t spin = (uint32_t)env_count("EMU_LL_SPIN_LIMIT", 1L << 22);
       err = launch_ll(algo == Algo::Ring, t, o, a, status, spin, p.grid, p.block, p.lds, s);
     } else {
       err = launch_stepwise(coll, algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);

@@ -160,8 +160,9 @@ def test_ll_communicator_runs_reduce_scatter_and_all_gather():
 
 @pytest.mark.parametrize("algo", ["ring", "tree"])
 def test_ll_abandoned_call_is_reported_and_the_next_call_is_right(algo, monkeypatch):
-    """Failure handling, forced from the host: EMU_LL_SPIN_LIMIT=1 makes
-    every wait give up after two polls, so the call abandons; every wave
+    """Failure handling, forced from the host: EMU_LL_SPIN_LIMIT=0 makes
+    every wait give up at its first poll that finds nothing ready, so the
+    call abandons; every wave
     still meets the workgroup barriers and the kernel ends.  The status word
     reports it, and the next call (normal limit; the FIFOs live in LDS and
     restart with every launch) is bit-exact again."""
@@ -178,14 +179,14 @@ def test_ll_abandoned_call_is_reported_and_the_next_call_is_right(algo, monkeypa
     abandoned = False
     for attempt in range(5):
         announce(f"LL {algo} forced abandon, attempt {attempt}")
-        monkeypatch.setenv("EMU_LL_SPIN_LIMIT", "1")
+        monkeypatch.setenv("EMU_LL_SPIN_LIMIT", "0")
         E.allreduce_tensors(sends, recvs, "sum")
         monkeypatch.delenv("EMU_LL_SPIN_LIMIT")
         torch.cuda.synchronize()
         if E.protocol_status():
             abandoned = True
             break
-    assert abandoned, "a spin limit of 1 never made a wait give up"
+    assert abandoned, "a spin limit of 0 never made a wait give up"
     assert not E.protocol_status()
     E.allreduce_tensors(sends, recvs, "sum")
     torch.cuda.synchronize()

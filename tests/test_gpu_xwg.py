@@ -195,8 +195,9 @@ def test_xwg_communicator_runs_reduce_scatter_and_all_gather(mode):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_xwg_abandoned_call_is_reported_and_recovered(mode, monkeypatch):
-    """Failure handling, forced from the host: EMU_XWG_SPIN_LIMIT=1 makes
-    every wait give up after two polls, so the call abandons (every
+    """Failure handling, forced from the host: EMU_XWG_SPIN_LIMIT=0 makes
+    every wait give up at its first poll that finds nothing ready, so the
+    call abandons (every
     workgroup still exits).  Until emu_protocol_status has reported it, a
     later call does nothing (the abandon word is sticky, the FIFO counters
     no longer match); the report clears the FIFOs, and the next call is
@@ -214,7 +215,7 @@ def test_xwg_abandoned_call_is_reported_and_recovered(mode, monkeypatch):
     abandoned = False
     for attempt in range(5):
         announce(f"{mode} forced abandon, attempt {attempt}")
-        monkeypatch.setenv("EMU_XWG_SPIN_LIMIT", "1")
+        monkeypatch.setenv("EMU_XWG_SPIN_LIMIT", "0")
         E.allreduce_tensors(sends, recvs, "sum")
         monkeypatch.delenv("EMU_XWG_SPIN_LIMIT")
         torch.cuda.synchronize()
@@ -230,7 +231,7 @@ def test_xwg_abandoned_call_is_reported_and_recovered(mode, monkeypatch):
             break
         # neither call abandoned: both completed, and the outputs are right
         assert np.array_equal(to_host_bits(recvs[0], "f32").view(np.uint8), want.view(np.uint8))
-    assert abandoned, "a spin limit of 1 never made a wait give up"
+    assert abandoned, "a spin limit of 0 never made a wait give up"
     assert not E.protocol_status()
     E.allreduce_tensors(sends, recvs, "sum")
     torch.cuda.synchronize()

@@ -2,7 +2,10 @@
 
 Workload: 8 virtual ranks on one node (the tree is the intra-node chain),
 12 channels, 512 KiB chunks, float32 sum, 16 Mi elements (64 MiB) per rank
-drawn from N(0, 1), all buffers resident in HBM before timing starts.
+drawn from N(0, 1), all buffers resident in HBM before timing starts.  By
+default the 16 rank buffers are carved from one pool at emu_buffer_layout's
+offsets, the placement the library provides for its virtual ranks;
+--placement torch gives each buffer its own torch allocation instead.
 
 One step = one pass of the whole path over the batch: ring and tree, each in
 the fused single-pass mode and in the stepwise mode (4 all-reduces, each
@@ -95,6 +98,9 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=16 * 1024 * 1024)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--placement", choices=("library", "torch"), default="library",
+                    help="library: the 2N rank buffers carved from one pool at emu_buffer_layout's offsets; "
+                         "torch: one torch allocation per buffer (all sends, then all receives)")
     ap.add_argument("--calibration-kernel", action="store_true",
                     help="also run one elementwise multiply over 512 MiB (read) + 512 MiB (write), "
                          "the known-size kernel that scales rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -120,8 +126,13 @@ def main() -> int:
     s_bytes = count * w.itemsize
     log(f"generating {n} x {count} f32 inputs")
     xs = I.rank_inputs(w)
-    sends = [torch.from_numpy(x).cuda() for x in xs]
-    recvs = [torch.empty_like(s) for s in sends]
+    if args.placement == "library":
+        pool, sends, recvs = E.rank_buffers(n, count, torch.float32)
+        for s_, x in zip(sends, xs):
+            s_.copy_(torch.from_numpy(x))
+    else:
+        sends = [torch.from_numpy(x).cuda() for x in xs]
+        recvs = [torch.empty_like(s) for s in sends]
     del xs
     stream = torch.cuda.current_stream()
     sptr = [t.data_ptr() for t in sends]
@@ -235,7 +246,9 @@ def main() -> int:
                                f"fused + stepwise",
                    "nranks": n, "nnodes": w.nnodes, "nchannels": w.nchannels,
                    "chunk_bytes": w.chunk_bytes, "count_per_rank": count, "global_batch": n * count,
-                   "parallelism": "single GPU, virtual ranks"},
+                   "parallelism": "single GPU, virtual ranks",
+                   "placement": "emu_buffer_layout pool" if args.placement == "library"
+                                else "one torch allocation per buffer"},
         "roofline": {"bound": "hbm", "kernel": d["kernel"], "leg": dominant,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

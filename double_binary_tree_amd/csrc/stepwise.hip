@@ -166,6 +166,9 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
       const uint32_t nelem = wave_u32<WAVE>(d.nelem), cell = wave_u32<WAVE>(d.first_cell);
       return {(uint64_t)cell * slice_elems, start, start + nelem};
     };
+    // A cell that lies wholly inside its block: every lane holds a whole
+    // vector, so no lane needs its bounds checked.
+    auto whole = [&](const View& w) { return w.start <= w.cell && w.cell + slice_elems <= w.end; };
     auto nbytes_of = [&](const View& w, uint64_t pos) -> int {
       if (pos < w.start || pos >= w.end) return 0;
       const uint64_t left = w.end - pos;
@@ -180,10 +183,15 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
       const void* src = a.send[me];
       if constexpr (WAVE) {
         const auto rs = buffer_view(static_cast<const char*>(src) + (w.cell * ESZ - load_shift));
+        if (enable && whole(w)) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const uint32_t lane = (uint32_t)((v * g + p) * unit);
-          x[v] = ld_buf(rs, enable && nbytes_of(w, w.cell + lane) == kVecBytes ? lane * ESZ : kNoLoad);
+          for (int v = 0; v < V; ++v) x[v] = ld_buf(rs, (uint32_t)((v * g + p) * kVecBytes));
+        } else {
+#pragma unroll
+          for (int v = 0; v < V; ++v) {
+            const uint32_t lane = (uint32_t)((v * g + p) * unit);
+            x[v] = ld_buf(rs, enable && nbytes_of(w, w.cell + lane) == kVecBytes ? lane * ESZ : kNoLoad);
+          }
         }
       } else {
 #pragma unroll
@@ -197,6 +205,7 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     auto fix_block = [&](uint32_t b, u32x4 (&x)[V]) {
       if constexpr (WAVE) {
         const View w = view_of(b);
+        if (w.cell + slice_elems <= w.end) return;   // a partial vector can only sit at the block end
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
@@ -208,6 +217,12 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
       const View w = view_of(b);
       void* dst = a.recv[me];
+      if (whole(w)) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          st_vec(dst, (w.cell + (uint32_t)((v * g + p) * unit)) * ESZ - store_shift, R::post(x[v]));
+        return;
+      }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
@@ -350,6 +365,11 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
     auto boff_of = [&](int q, int v) -> uint64_t { return pos_of(q, v) * ESZ; };
+    // Every slice but the first and the last lies inside the task: each lane
+    // holds a whole vector there, so a store needs no per-lane bounds.  (The
+    // same shortcut for the loads was slower on small messages: the loads'
+    // offsets are a select already, and the branch only lengthens a stage.)
+    auto interior = [&](int q) { return q > 0 && q + 1 < nslices; };
     // Under WAVE a slice is read with a buffer view based at its cell (whole
     // vectors without a branch, other lanes read zeros) and a partial vector
     // at the task end is read when it is consumed (fix_slice), as in the ring.
@@ -372,6 +392,7 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
     };
     auto fix_slice = [&](int q, u32x4 (&x)[V]) {
       if constexpr (WAVE) {
+        if (q + 1 < nslices) return;   // a partial vector can only sit at the task end
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const int nb = nbytes_of(q, v);
@@ -380,6 +401,11 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
       }
     };
     auto store_slice = [&](int q, const u32x4 (&x)[V]) {
+      if (interior(q)) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) st_vec(a.recv[r], boff_of(q, v), R::post(x[v]));
+        return;
+      }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int nb = nbytes_of(q, v);

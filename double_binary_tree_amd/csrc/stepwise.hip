@@ -375,8 +375,10 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
     // at the task end is read when it is consumed (fix_slice), as in the ring.
     auto load_slice = [&](int q, u32x4 (&x)[V], bool enable) {
       if constexpr (WAVE) {
-        const auto rs = buffer_view(static_cast<const char*>(a.send[r]) + pos_of(q, 0) * ESZ -
-                                    (uint64_t)p * kVecBytes);
+        // The cell's first byte, computed from uniform values only, so that
+        // the view sits in scalar registers (a base computed per lane would
+        // make the compiler loop over the distinct bases of the wave).
+        const auto rs = buffer_view(static_cast<const char*>(a.send[r]) + (first_cell + (uint64_t)q) * slice_elems * ESZ);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const uint32_t lane = (uint32_t)((v * g + p) * kVecBytes);

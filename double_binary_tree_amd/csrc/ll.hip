@@ -159,11 +159,11 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
     const RingTask task = tasks[t];
     const uint32_t me = __builtin_amdgcn_readfirstlane(orders[(size_t)task.ring * kMaxRanks + r]);
     // block b of this task: its cell and [start, end) range (scalar loads)
-    struct View { uint64_t pos, start, end; };
+    struct View { uint64_t cell, pos, start, end; };
     auto view_of = [&](uint32_t b) -> View {
       const RingLoopBlock d = loops[(size_t)task.loop * n + b];
-      return {((uint64_t)d.first_cell + task.slice) * slice_elems + (uint64_t)p * unit, d.offset,
-              d.offset + d.nelem};
+      const uint64_t cell = ((uint64_t)d.first_cell + task.slice) * slice_elems;
+      return {cell, cell + (uint64_t)p * unit, d.offset, d.offset + d.nelem};
     };
     auto nbytes_of = [&](const View& w) -> int {
       if (w.pos < w.start || w.pos >= w.end) return 0;
@@ -177,6 +177,10 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
     };
     auto store = [&](uint32_t b, const u32x4& x) {
       const View w = view_of(b);
+      if (w.start <= w.cell && w.cell + slice_elems <= w.end) {   // whole cell: no lane is out of range
+        st_vec(a.recv[me], w.pos * ESZ, R::post(x));
+        return;
+      }
       const int nb = nbytes_of(w);
       if (nb) st_any(a.recv[me], w.pos * ESZ, nb, R::post(x));
     };
@@ -283,6 +287,10 @@ __global__ __launch_bounds__(1024) void ll_tree(const StepArgs a, const TreeTask
       return nb ? ld_any(a.send[r], pos_of(q) * ESZ, nb) : u32x4{0, 0, 0, 0};
     };
     auto store = [&](int q, const u32x4& x) {
+      if (q > 0 && q + 1 < nslices) {   // inside the task: every lane holds a whole vector
+        st_vec(a.recv[r], pos_of(q) * ESZ, R::post(x));
+        return;
+      }
       const int nb = nbytes_of(q);
       if (nb) st_any(a.recv[r], pos_of(q) * ESZ, nb, R::post(x));
     };

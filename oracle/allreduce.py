@@ -56,13 +56,29 @@ def allreduce(inputs: list[np.ndarray], nnodes: int, algo: str, nchannels: int,
     ``stats``, if given, receives ``sent_elems`` (per-rank elements sent).
     """
     n, count = _check_inputs(inputs, dtype)
+    outputs = [np.array(x, copy=True) for x in inputs]
+    sent = [0] * n
+    topo = topology.build_topology(n, nnodes, nchannels, pattern, intra)
+    for c in range(nchannels):
+        allreduce_channel(inputs, outputs, c, topo, algo, chunk_bytes, dtype, op, unit_bytes, sent)
+    if stats is not None:
+        stats["sent_elems"] = sent
+    return outputs
+
+
+def allreduce_channel(inputs: list[np.ndarray], outputs: list[np.ndarray], c: int, topo, algo: str,
+                      chunk_bytes: int, dtype: str, op: str, unit_bytes: int = UNIT_BYTES,
+                      sent: list[int] | None = None) -> None:
+    """Channel c's part of the all-reduce: writes its element range of every
+    rank's ``outputs``; the channels' ranges are disjoint, so they can be
+    computed in any order (or at the same time).  ``topo`` is the
+    communicator's :func:`oracle.topology.build_topology`."""
+    n, count = _check_inputs(inputs, dtype)
     esz = numerics.ITEMSIZE[dtype]
     unit = _element_unit(dtype, unit_bytes)
     if chunk_bytes % esz:
         raise ValueError("chunk_bytes must hold whole elements")
     chunk_count = chunk_bytes // esz
-    outputs = [np.array(x, copy=True) for x in inputs]
-    sent = [0] * n
 
     def comb(a, b):
         return numerics.combine(dtype, op, a, b)
@@ -70,31 +86,27 @@ def allreduce(inputs: list[np.ndarray], nnodes: int, algo: str, nchannels: int,
     def cp(a):
         return np.array(a, copy=True)
 
-    topo = topology.build_topology(n, nnodes, nchannels, pattern, intra)
+    grid_offset, ch_count = partition.channel_ranges(count, unit, topo.nchannels)[c]
     if algo == "ring":
-        for c, (grid_offset, ch_count) in enumerate(partition.channel_ranges(count, unit, nchannels)):
-            order = topo.channels[c].order
-            for blocks in partition.ring_loops(grid_offset, ch_count, n, chunk_count, unit):
-                bufs = [[inputs[order[p]][o:o + ln].copy() for (o, ln) in blocks] for p in range(n)]
-                pos_sent = [0] * n
-                ring.ring_allreduce_blocks(bufs, comb, cp, sent=pos_sent, size=len)
-                for p in range(n):
+        order = topo.channels[c].order
+        for blocks in partition.ring_loops(grid_offset, ch_count, n, chunk_count, unit):
+            bufs = [[inputs[order[p]][o:o + ln].copy() for (o, ln) in blocks] for p in range(n)]
+            pos_sent = [0] * n
+            ring.ring_allreduce_blocks(bufs, comb, cp, sent=pos_sent, size=len)
+            for p in range(n):
+                if sent is not None:
                     sent[order[p]] += pos_sent[p]
-                    for (o, ln), blk in zip(blocks, bufs[p]):
-                        outputs[order[p]][o:o + ln] = blk
+                for (o, ln), blk in zip(blocks, bufs[p]):
+                    outputs[order[p]][o:o + ln] = blk
     elif algo == "tree":
-        for c, (grid_offset, ch_count) in enumerate(partition.channel_ranges(count, unit, nchannels)):
-            ch = topo.channels[c]
-            for o, ln in partition.tree_chunks(grid_offset, ch_count, chunk_count):
-                res = tree.tree_allreduce_chunk([inputs[r][o:o + ln] for r in range(n)],
-                                                ch.up, ch.down, comb, cp, sent=sent, size=len)
-                for r in range(n):
-                    outputs[r][o:o + ln] = res[r]
+        ch = topo.channels[c]
+        for o, ln in partition.tree_chunks(grid_offset, ch_count, chunk_count):
+            res = tree.tree_allreduce_chunk([inputs[r][o:o + ln] for r in range(n)],
+                                            ch.up, ch.down, comb, cp, sent=sent, size=len)
+            for r in range(n):
+                outputs[r][o:o + ln] = res[r]
     else:
         raise ValueError(f"unknown algo {algo}")
-    if stats is not None:
-        stats["sent_elems"] = sent
-    return outputs
 
 
 def allreduce_at(inputs: list[np.ndarray], index: np.ndarray, nnodes: int, algo: str,

@@ -10,19 +10,18 @@ Sources (page title, then section / figure):
     neighbour; in reduce-scatter the receiver adds it to its own block, in
     all-gather the receiver overwrites its block with the finished sum);
   - section "推导 / 关键公式" (each rank sends 2(n-1) blocks of S/n);
-  - section "手撕代码" (at reduce-scatter step s rank r sends block (r-s) mod n
-    to rank r+1; at all-gather step s it sends block (r+1-s) mod n; every rank
-    copies what it sends before any receiver applies its update, so all sends
-    of a step read the values from before that step).
+  - section "手撕代码" (the same schedule simulated step by step: all sends of
+    a step read the values from before that step).
 * "NCCL 内部机制：一次 AllReduce 如何变成拓扑图、Channel 与 GPU Kernel", section
   "Ring：带宽友好，但启动步骤会随规模增长" (first step sends, middle steps
   receive-reduce-send, the last reduce-scatter step also writes the result,
   then the finished blocks are forwarded around the ring).
 
-The simulator moves whole blocks between per-rank block lists.  It is
-generic in what a block is: numpy arrays with the rounding ``combine`` of
-``numerics`` for numbers, or frozensets with set union for the symbolic
-contributor tables of Figure 1.
+The simulator follows each block along its route round the ring (the
+positions it visits, one hop per step) and moves whole blocks between
+per-position block lists.  It is generic in what a block is: numpy arrays
+with the rounding ``combine`` of ``numerics`` for numbers, or frozensets
+with set union for the symbolic contributor tables of Figure 1.
 
 Consequence used by the tests: block k's value is the left fold that starts
 at rank k and walks the ring, x_k, x_{k+1}, ..., x_{k-1}, each hop rounded.
@@ -35,42 +34,53 @@ from __future__ import annotations
 from typing import Any, Callable
 
 
+def ring_route(n: int, k: int) -> list[int]:
+    """The positions block k visits in the reduce-scatter: it starts at
+    position k (Figure 1: every rank first sends its own block) and moves
+    one position along the ring, p -> p+1, at every step."""
+    return [(k + j) % n for j in range(n)]
+
+
 def ring_reduce_scatter_steps(bufs: list[list[Any]], combine: Callable[[Any, Any], Any],
                               copy: Callable[[Any], Any], trace: list | None = None,
                               sent: list[int] | None = None, size: Callable[[Any], int] | None = None) -> None:
-    """The n-1 reduce-scatter steps, in place on ``bufs[r][b]`` (position r,
-    block b): at step s every position r sends block (r-s) mod n to r+1,
-    which adds it to its own copy of that block; all sends of a step read the
-    values from before the step.  Afterwards position r holds the full
-    reduction of block (r+1) mod n.  ``trace``/``sent``/``size`` as in
+    """The n-1 reduce-scatter steps, in place on ``bufs[p][b]`` (position p,
+    block b).  At step j every block b takes one hop of its route: the
+    position that holds its partial so far, route[j-1], passes it on to
+    route[j], which folds it into its own copy (own (op) incoming, rounded).
+    One step's hops write cells (route[j], b) and read cells (route[j-1], b),
+    never a cell another hop of the step writes, so every hop sees the
+    values from before the step.  Afterwards position p holds the full
+    reduction of block p+1 (mod n).  ``trace``/``sent``/``size`` as in
     :func:`ring_allreduce_blocks`."""
     n = len(bufs)
-    for s in range(n - 1):
-        outgoing = [copy(bufs[r][(r - s) % n]) for r in range(n)]
-        for r in range(n):
-            dst, b = (r + 1) % n, (r - s) % n
-            bufs[dst][b] = combine(bufs[dst][b], outgoing[r])
+    routes = [ring_route(n, b) for b in range(n)]
+    for j in range(1, n):
+        for b in range(n):
+            src, dst = routes[b][j - 1], routes[b][j]
+            incoming = copy(bufs[src][b])
+            bufs[dst][b] = combine(bufs[dst][b], incoming)
             if sent is not None:
-                sent[r] += size(outgoing[r])
+                sent[src] += size(incoming)
         if trace is not None:
-            trace.append((("RS", s + 1), [[copy(b) for b in row] for row in bufs]))
+            trace.append((("RS", j), [[copy(x) for x in row] for row in bufs]))
 
 
 def ring_all_gather_steps(bufs: list[list[Any]], copy: Callable[[Any], Any], trace: list | None = None,
                           sent: list[int] | None = None, size: Callable[[Any], int] | None = None) -> None:
-    """The n-1 all-gather steps, in place: position r starts with (at least)
-    block (r+1) mod n; at step s it sends block (r+1-s) mod n to r+1, which
-    overwrites its copy.  Afterwards every position holds every block."""
+    """The n-1 all-gather steps, in place: the finished block b sits at the
+    end of its reduce-scatter route, position b-1 (mod n); at step j it
+    moves on from position b+j-2 to b+j-1, which overwrites its copy.
+    Afterwards every position holds every block."""
     n = len(bufs)
-    for s in range(n - 1):
-        outgoing = [copy(bufs[r][(r + 1 - s) % n]) for r in range(n)]
-        for r in range(n):
-            dst, b = (r + 1) % n, (r + 1 - s) % n
-            bufs[dst][b] = outgoing[r]
+    for j in range(1, n):
+        for b in range(n):
+            src, dst = (b + j - 2) % n, (b + j - 1) % n
+            bufs[dst][b] = copy(bufs[src][b])
             if sent is not None:
-                sent[r] += size(outgoing[r])
+                sent[src] += size(bufs[dst][b])
         if trace is not None:
-            trace.append((("AG", s + 1), [[copy(b) if b is not None else None for b in row] for row in bufs]))
+            trace.append((("AG", j), [[copy(x) if x is not None else None for x in row] for row in bufs]))
 
 
 def ring_allreduce_blocks(bufs: list[list[Any]], combine: Callable[[Any, Any], Any],

@@ -59,64 +59,63 @@ from __future__ import annotations
 from dataclasses import dataclass, field
 
 
-def btree(n: int, r: int) -> tuple[int, int, int, int | None]:
-    """Node-level binary tree over node indices 0..n-1.
-
-    Returns ``(parent, child0, child1, child_type)``.  Node 0 is the root and
-    has only the second child.  For r > 0, with b the lowest set bit of r, the
-    preferred parent clears b and sets the next higher bit; if that index does
-    not exist the parent only clears b.  The children sit b/2 below and b/2
-    above r; the upper child shrinks its offset by halves until it names an
-    existing node.  ``child_type`` says whether r lies below (0) or above (1)
-    its parent.  (Section "Btree 的 bit 构造".)
-    """
+def btree_parent(n: int, r: int) -> int:
+    """Parent of node r in the node-level binary tree over 0..n-1 (-1 for
+    the root, node 0).  Section "Btree 的 bit 构造": with b the lowest set bit
+    of r, the parent is the node one level up, whose lowest set bit is 2b:
+    of the two neighbours r - b and r + b that is the one with bit 2b set
+    (clear bit b of r, set bit 2b).  When that node does not exist (r + b >=
+    n) the parent is r - b (bit b cleared, nothing set)."""
     if not (0 <= r < n):
         raise ValueError(f"rank {r} outside 0..{n - 1}")
-    bit = 1
-    while bit < n and not (bit & r):
-        bit <<= 1
     if r == 0:
-        # The scan found no set bit: bit is now the smallest power of two >= n.
-        return -1, -1, (bit >> 1) if n > 1 else -1, None
-    parent = (r ^ bit) | (bit << 1)
-    if parent >= n:
-        parent = r ^ bit
-    child_type = 0 if r < parent else 1
-    half = bit >> 1
-    child0 = r - half if half > 0 else -1
-    child1 = -1
-    offset = half
-    while offset > 0:
-        if r + offset < n:
-            child1 = r + offset
-            break
-        offset >>= 1
+        return -1
+    b = r & -r
+    up = r - b if r & (2 * b) else r + b
+    return up if up < n else r - b
+
+
+def btree(n: int, r: int) -> tuple[int, int, int, int | None]:
+    """Node r of the node-level binary tree over 0..n-1.
+
+    Returns ``(parent, child0, child1, child_type)``.  The tree is the one
+    the parent rule of :func:`btree_parent` defines; the children of r are
+    the nodes whose parent r is, at most one below r (child0) and one above
+    (child1).  ``child_type`` says whether r lies below (0) or above (1) its
+    parent; None at the root.  (Section "Btree 的 bit 构造": node 0 is the
+    root with only its second child.)
+    """
+    parent = btree_parent(n, r)
+    below = [x for x in range(n) if x < r and btree_parent(n, x) == r]
+    above = [x for x in range(n) if x > r and btree_parent(n, x) == r]
+    if len(below) > 1 or len(above) > 1:
+        raise TopologyError(f"node {r} of {n} would have more than one child on a side")
+    child0 = below[0] if below else -1
+    child1 = above[0] if above else -1
+    child_type = None if parent == -1 else (0 if r < parent else 1)
     return parent, child0, child1, child_type
 
 
 def dtree(n: int, r: int):
     """The two node-level trees of node r.
 
-    Tree 0 is :func:`btree`.  Tree 1 is the same construction evaluated at a
-    relabelled index and mapped back: for odd n the index is shifted down by
-    one (mod n) and results shifted up by one; for even n the index is
-    mirrored (x -> n-1-x) both ways.  The child type of tree 1 is the one
-    computed in the relabelled coordinates.  (Section "双树：偶数 mirror，奇数
-    shift".)
+    Tree 0 is :func:`btree`.  Tree 1 is tree 0 with its node ids relabelled
+    by sigma: x -> n-1-x (mirror) for even n, x -> x+1 mod n (shift) for odd
+    n.  So node r of tree 1 is node sigma^-1(r) of tree 0 with every id it
+    names mapped through sigma; the child slots and the child type carry
+    over unchanged.  (Section "双树：偶数 mirror，奇数 shift".)
     """
-    t0 = btree(n, r)
     if n % 2 == 1:
-        p, c0, c1, ct = btree(n, (r - 1 + n) % n)
-
-        def back(x):
-            return -1 if x == -1 else (x + 1) % n
+        def sigma(x):
+            return (x + 1) % n
+        source = (r - 1) % n
     else:
-        p, c0, c1, ct = btree(n, n - 1 - r)
-
-        def back(x):
-            return -1 if x == -1 else n - 1 - x
-    t1 = (back(p), back(c0), back(c1), ct)
-    return t0, t1
+        def sigma(x):
+            return n - 1 - x
+        source = n - 1 - r
+    p, c0, c1, ct = btree(n, source)
+    t1 = tuple(-1 if x == -1 else sigma(x) for x in (p, c0, c1)) + (ct,)
+    return btree(n, r), t1
 
 
 def log2i(x: int) -> int:

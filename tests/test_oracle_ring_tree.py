@@ -59,6 +59,29 @@ def test_two_rank_example_ring_and_tree():
         assert [o.tolist() for o in out] == want, (algo, nnodes)
 
 
+@pytest.mark.parametrize("n,count", [(2, 7), (3, 10), (4, 1024), (5, 101), (8, 999), (9, 64)])
+def test_ring_with_unit_one_is_the_per_block_left_fold(n, count):
+    # Interview page, section "手撕代码": each rank's vector is cut into n parts
+    # the numpy.array_split way, and part k is reduced along the ring starting
+    # at rank k.  With a unit of one element, one channel and one loop, the
+    # oracle's step simulation must equal that closed form element by
+    # element: acc = x_k; acc = rnd(acc + x_{k+j mod n}) for j = 1 .. n-1,
+    # every add a plain IEEE single add (numpy float32 scalars).
+    rng = np.random.default_rng(100 + n)
+    xs = [rng.standard_normal(count).astype(np.float32) for _ in range(n)]
+    out = A.allreduce(xs, 1, "ring", 1, 4 * count, "f32", "sum", unit_bytes=4)
+    parts = np.array_split(np.arange(count), n)
+    want = np.empty(count, dtype=np.float32)
+    for k, idx in enumerate(parts):
+        for i in idx:
+            acc = np.float32(xs[k][i])
+            for j in range(1, n):
+                acc = np.float32(acc + xs[(k + j) % n][i])
+            want[i] = acc
+    for o in out:
+        assert np.array_equal(o.view(np.uint32), want.view(np.uint32))
+
+
 def _order_pin(tag):
     vals = {}
     for line in golden_lines("order_pins_f32.txt"):

@@ -10,42 +10,58 @@
 
 namespace emu {
 
-NodeTreeEdges node_btree(int n, int r) {
-  // Lowest set bit of r among the powers of two below n; for r = 0 the scan
-  // runs through and ends at the smallest power of two >= n.
-  int bit = 1;
-  while (bit < n && !(bit & r)) bit <<= 1;
-  if (r == 0) return {-1, -1, n > 1 ? (bit >> 1) : -1, -1};
-  int parent = (r ^ bit) | (bit << 1);   // clear the low bit, set the next one
-  if (parent >= n) parent = r ^ bit;       // that node does not exist: only clear
-  NodeTreeEdges e;
-  e.parent = parent;
-  e.child_type = r < parent ? 0 : 1;
-  const int half = bit >> 1;
-  e.child0 = half > 0 ? r - half : -1;
-  e.child1 = -1;
-  for (int off = half; off > 0; off >>= 1) {   // upper child: shrink until it exists
-    if (r + off < n) { e.child1 = r + off; break; }
+namespace {
+
+// Hangs node m, reached with span s, below `parent`, then its subtree: the
+// lower child sits s/2 below m, the upper child t above m for the largest
+// power of two t <= s/2 that still names a node; the children's spans are
+// s/2 and t.
+void hang(std::vector<NodeTreeEdges>& t, int n, int parent, int m, int span, int type) {
+  t[m] = {parent, -1, -1, type};
+  const int half = span / 2;
+  if (half == 0) return;
+  t[m].child0 = m - half;   // m is a multiple of span, so m - half >= 0
+  hang(t, n, m, m - half, half, 0);
+  int up = half;
+  while (up > 0 && m + up >= n) up /= 2;
+  if (up > 0) {
+    t[m].child1 = m + up;
+    hang(t, n, m, m + up, up, 1);
   }
-  return e;
 }
 
-std::array<NodeTreeEdges, 2> node_dtree(int n, int r) {
-  std::array<NodeTreeEdges, 2> t;
-  t[0] = node_btree(n, r);
-  NodeTreeEdges s;
-  if (n % 2 == 1) {
-    // odd: build at r-1 (mod n), move every id up by one
-    s = node_btree(n, (r - 1 + n) % n);
-    auto back = [n](int x) { return x < 0 ? -1 : (x + 1) % n; };
-    s.parent = back(s.parent); s.child0 = back(s.child0); s.child1 = back(s.child1);
-  } else {
-    // even: build at the mirrored index n-1-r, mirror the ids back
-    s = node_btree(n, n - 1 - r);
-    auto back = [n](int x) { return x < 0 ? -1 : n - 1 - x; };
-    s.parent = back(s.parent); s.child0 = back(s.child0); s.child1 = back(s.child1);
+}  // namespace
+
+// The node-level binary tree, top down.  The bit construction of the pages
+// puts node r (lowest set bit b) at height log2(b): its parent is the nearer
+// node of the next height, its children sit at r -/+ b/2.  Read from the
+// root down that is a nest of power-of-two halves: node 0 is the root and
+// has one child, the largest power of two p below n, which spans (0, 2p);
+// every node splits what it spans into a lower and an upper half and
+// hangs the middle node of each.  Where the upper half runs past n its
+// middle node moves down to the largest power-of-two offset that exists.
+std::vector<NodeTreeEdges> node_btree(int n) {
+  std::vector<NodeTreeEdges> t(n > 0 ? n : 0, NodeTreeEdges{-1, -1, -1, -1});
+  if (n <= 1) return t;
+  int p = 1;
+  while (2 * p < n) p *= 2;
+  t[0].child1 = p;
+  hang(t, n, 0, p, p, 1);
+  return t;
+}
+
+// The double binary tree: tree 1 is tree 0 with every node index relabelled
+// (mirror x -> n-1-x for even n, shift x -> x+1 mod n for odd n), child
+// slots and child types carried over unchanged.
+std::array<std::vector<NodeTreeEdges>, 2> node_dtree(int n) {
+  std::array<std::vector<NodeTreeEdges>, 2> t;
+  t[0] = node_btree(n);
+  auto relabel = [n](int x) { return x < 0 ? -1 : (n % 2 == 1 ? (x + 1) % n : n - 1 - x); };
+  t[1].assign(t[0].size(), NodeTreeEdges{-1, -1, -1, -1});
+  for (int x = 0; x < n; ++x) {
+    const NodeTreeEdges& e = t[0][x];
+    t[1][relabel(x)] = {relabel(e.parent), relabel(e.child0), relabel(e.child1), e.child_type};
   }
-  t[1] = s;
   return t;
 }
 
@@ -133,8 +149,7 @@ int build_topology(int nranks, int nnodes, int nchannels, int pattern, const int
   topo.nchannels = nchannels;
   topo.pattern = pattern;
   topo.depth_approx = L - 1 + log2_floor(nnodes);
-  std::vector<std::array<NodeTreeEdges, 2>> node_trees(nnodes);
-  for (int m = 0; m < nnodes; ++m) node_trees[m] = node_dtree(nnodes, m);
+  const std::array<std::vector<NodeTreeEdges>, 2> node_trees = node_dtree(nnodes);
   const int first_half = (nchannels + 1) / 2;
   for (int c = 0; c < nchannels; ++c) {
     ChannelTopology ch;
@@ -155,7 +170,7 @@ int build_topology(int nranks, int nnodes, int nchannels, int pattern, const int
     // parent node's child0 or child1 head (by child type); a child head
     // takes the child node's parent head, child0 before child1.
     for (int node = 0; node < nnodes; ++node) {
-      const NodeTreeEdges& e = node_trees[node][ch.tree_index];
+      const NodeTreeEdges& e = node_trees[ch.tree_index][node];
       if (e.parent != -1) ch.ranks[at(node, pos[0])].up = at(e.parent, pos[1 + e.child_type]);
       if (e.child0 != -1 && !attach_down(ch.ranks[at(node, pos[1])], at(e.child0, pos[0]))) return EMU_ERR_INTERNAL;
       if (e.child1 != -1 && !attach_down(ch.ranks[at(node, pos[2])], at(e.child1, pos[0]))) return EMU_ERR_INTERNAL;

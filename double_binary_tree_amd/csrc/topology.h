@@ -16,12 +16,12 @@ struct NodeTreeEdges {
   int child_type;  // 0: below its parent, 1: above; -1 at the root
 };
 
-// Binary tree over node indices 0..n-1 (page "NCCL 专家课程 13", section
-// "Btree 的 bit 构造").
-NodeTreeEdges node_btree(int n, int r);
-// Tree 0 and tree 1 of the double binary tree (section "双树：偶数 mirror，
-// 奇数 shift").
-std::array<NodeTreeEdges, 2> node_dtree(int n, int r);
+// Binary tree over node indices 0..n-1, one entry per node (page "NCCL 专家
+// 课程 13", section "Btree 的 bit 构造").
+std::vector<NodeTreeEdges> node_btree(int n);
+// Tree 0 and tree 1 of the double binary tree, one entry per node each
+// (section "双树：偶数 mirror，奇数 shift").
+std::array<std::vector<NodeTreeEdges>, 2> node_dtree(int n);
 
 struct RankRecord {
   int up = -1;

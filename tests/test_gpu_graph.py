@@ -14,8 +14,7 @@ import pytest
 
 from double_binary_tree_amd import inputs as I
 from oracle import allreduce as A
-from tests.gpu_util import announce, run_allreduce, to_device, to_host_bits
-from tests.test_gpu_fullsize import _sample
+from tests.gpu_util import announce, check_every_element, clear_inputs, run_allreduce
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +50,7 @@ def _gpu():
     from double_binary_tree_amd import emucomm as E
     E.lib()
     yield
+    clear_inputs()
     E.comm_destroy()
     torch.cuda.empty_cache()
 
@@ -98,35 +98,11 @@ def test_graph_parity_edge_counts(name, algo, mode):
         _check(name, algo, mode, count, chunk_bytes=64, inplace=False, salt=2)
 
 
-@pytest.mark.parametrize("name", ["split4x8_f16", "orders8_f32", "table4_bf16"])
-def test_graph_full_size_sampled(name):
-    # The workload's full size and chunk, checked on sampled positions; every
-    # rank holds the same bits and the two modes agree everywhere.
-    import torch
-    from double_binary_tree_amd import emucomm as E
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+@pytest.mark.parametrize("name", ["split4x8_f16", "orders8_f32", "table4_bf16", "balanced4x8_f32max"])
+def test_graph_full_size_every_element(name, algo):
+    # The workload's full size and chunk with the graph's pattern and
+    # per-channel orders: every element of every rank equals the oracle's,
+    # fused and stepwise, out of place and in place.
     w, pattern, intra = GRAPHS[name]
-    announce(f"graph full size {name}: {w.nranks} ranks x {w.count} {w.dtype} pattern={pattern}")
-    xs = I.rank_inputs(w)
-    idx = _sample(w, w.count, np.random.default_rng(6))
-    sends = [to_device(x, w.dtype) for x in xs]
-    for algo in ("ring", "tree"):
-        want = A.allreduce_at(xs, idx, w.nnodes, algo, w.nchannels, w.chunk_bytes, w.dtype, w.op,
-                              pattern=pattern, intra=intra)
-        outs = {}
-        for mode in ("fused", "stepwise"):
-            announce(f"  {name} {algo} {mode}")
-            E.comm_init(w.nranks, w.nnodes, algo, w.nchannels, w.chunk_bytes, mode=mode, pattern=pattern, intra=intra)
-            recvs = [torch.empty_like(s) for s in sends]
-            E.allreduce_tensors(sends, recvs, w.op)
-            torch.cuda.synchronize()
-            flat = [r.view(torch.uint8) for r in recvs]
-            for r in flat[1:]:
-                assert torch.equal(r, flat[0]), f"{name} {algo} {mode}: ranks differ"
-            got = to_host_bits(recvs[0], w.dtype)[idx]
-            assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"{name} {algo} {mode}: sampled outputs"
-            outs[mode] = flat[0]
-            del recvs, flat
-        assert torch.equal(outs["fused"], outs["stepwise"]), f"{name} {algo}: modes differ"
-        del outs
-    del sends
-    torch.cuda.empty_cache()
+    check_every_element(w, algo, pattern=pattern, intra=intra, label=f"graph {name} ")

@@ -12,7 +12,7 @@ import pytest
 
 from double_binary_tree_amd import inputs as I
 from oracle import allreduce as A
-from tests.gpu_util import announce, run_allreduce, to_device, to_host_bits
+from tests.gpu_util import announce, check_every_element, clear_inputs, run_allreduce, to_device, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +26,7 @@ def _gpu():
     E.lib()
     assert not E.protocol_status()
     yield
+    clear_inputs()
     E.comm_destroy()
     torch.cuda.empty_cache()
 
@@ -96,40 +97,13 @@ def test_ll_shapes(n, m, nch, algo):
     _check(w, algo, 6 * 1024 + 13, chunk_bytes=256, inplace=False)
 
 
+@pytest.mark.parametrize("algo", ["ring", "tree"])
 @pytest.mark.parametrize("name", ["chain8_f32", "dtree16_bf16", "dtree15_bf16"])
-def test_ll_full_size_equals_slot_protocol(name):
-    """At full size (the workload's own launch configuration): the LL result
-    equals the slot protocol's bit for bit on every element (that result is
-    held to the oracle by the full-size parity tests), every rank holds the
-    same bits, and sampled positions equal the oracle's."""
-    import torch
-    from double_binary_tree_amd import emucomm as E
-    w = I.WORKLOADS[name]
-    xs = I.rank_inputs(w)
-    rng = np.random.default_rng(9)
-    idx = np.unique(np.concatenate([rng.integers(0, w.count, 2048), [0, w.count - 1]])).astype(np.int64)
-    sends = [to_device(x, w.dtype) for x in xs]
-    for algo in w.algos:
-        announce(f"LL full size {name} {algo}")
-        want = A.allreduce_at(xs, idx, w.nnodes, algo, w.nchannels, w.chunk_bytes, w.dtype, w.op)
-        outs = {}
-        for mode in ("stepwise", "ll"):
-            E.comm_init(w.nranks, w.nnodes, algo, w.nchannels, w.chunk_bytes, mode=mode)
-            recvs = [torch.empty_like(s) for s in sends]
-            E.allreduce_tensors(sends, recvs, w.op)
-            torch.cuda.synchronize()
-            flat = [r.view(torch.uint8) for r in recvs]
-            for r in flat[1:]:
-                assert torch.equal(r, flat[0]), f"{name} {algo} {mode}: ranks differ"
-            outs[mode] = flat[0]
-            del recvs, flat
-        _not_abandoned()
-        assert torch.equal(outs["ll"], outs["stepwise"]), f"{name} {algo}: LL differs from the slot protocol"
-        got = to_host_bits(outs["ll"].view(sends[0].dtype), w.dtype)[idx]
-        assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"{name} {algo}: differs from the oracle"
-        del outs
-    del sends
-    torch.cuda.empty_cache()
+def test_ll_full_size_every_element(name, algo):
+    """At full size (the workload's own launch configuration), with the LL
+    protocol: every element of every rank equals the oracle's, out of place
+    and in place, and no call is abandoned."""
+    check_every_element(I.WORKLOADS[name], algo, modes=("ll",), label="LL ")
 
 
 def test_ll_communicator_runs_reduce_scatter_and_all_gather():
@@ -179,9 +153,11 @@ def test_ll_abandoned_call_is_reported_and_the_next_call_is_right(algo, monkeypa
     abandoned = False
     for attempt in range(5):
         announce(f"LL {algo} forced abandon, attempt {attempt}")
+        monkeypatch.setenv("EMU_DEBUG", "2")      # the library reads test hooks only in debug mode
         monkeypatch.setenv("EMU_LL_SPIN_LIMIT", "0")
         E.allreduce_tensors(sends, recvs, "sum")
         monkeypatch.delenv("EMU_LL_SPIN_LIMIT")
+        monkeypatch.delenv("EMU_DEBUG")
         torch.cuda.synchronize()
         if E.protocol_status():
             abandoned = True

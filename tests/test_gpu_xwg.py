@@ -14,7 +14,7 @@ import pytest
 
 from double_binary_tree_amd import inputs as I
 from oracle import allreduce as A
-from tests.gpu_util import announce, run_allreduce, to_device, to_host_bits
+from tests.gpu_util import announce, check_every_element, clear_inputs, run_allreduce, to_device, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +30,7 @@ def _gpu():
     E.lib()
     assert not E.protocol_status()
     yield
+    clear_inputs()
     E.comm_destroy()
     torch.cuda.empty_cache()
 
@@ -119,37 +120,13 @@ def test_xwg_counters_continue_across_calls(mode):
 
 @pytest.mark.parametrize("name", ["chain8_f32", "dtree16_bf16", "hier4x8_f16"])
 @pytest.mark.parametrize("mode", MODES)
-def test_xwg_full_size_equals_in_workgroup_ring(name, mode):
-    """At full size (the workload's own channels and chunk): the result
-    equals the one-workgroup stepwise ring's bit for bit on every element
-    (that result is held to the oracle by the full-size parity tests), every
-    rank holds the same bits, and sampled positions equal the oracle's."""
-    import torch
+def test_xwg_full_size_every_element(name, mode):
+    """At full size (the workload's own channels and chunk), with the FIFOs
+    in device memory: every element of every rank equals the oracle's ring
+    result, out of place and in place, and no call is abandoned."""
     from double_binary_tree_amd import emucomm as E
-    w = I.WORKLOADS[name]
-    xs = I.rank_inputs(w)
-    rng = np.random.default_rng(11)
-    idx = np.unique(np.concatenate([rng.integers(0, w.count, 2048), [0, w.count - 1]])).astype(np.int64)
-    sends = [to_device(x, w.dtype) for x in xs]
-    announce(f"{mode} full size {name} ring")
-    want = A.allreduce_at(xs, idx, w.nnodes, "ring", w.nchannels, w.chunk_bytes, w.dtype, w.op)
-    outs = {}
-    for m in ("stepwise", mode):
-        E.comm_init(w.nranks, w.nnodes, "ring", w.nchannels, w.chunk_bytes, mode=m)
-        recvs = [torch.empty_like(s) for s in sends]
-        E.allreduce_tensors(sends, recvs, w.op)
-        torch.cuda.synchronize()
-        flat = [r.view(torch.uint8) for r in recvs]
-        for r in flat[1:]:
-            assert torch.equal(r, flat[0]), f"{name} {m}: ranks differ"
-        outs[m] = flat[0]
-        del recvs, flat
-    _not_abandoned()
-    assert torch.equal(outs[mode], outs["stepwise"]), f"{name} {mode}: differs from the in-workgroup ring"
-    got = to_host_bits(outs[mode].view(sends[0].dtype), w.dtype)[idx]
-    assert np.array_equal(got.view(np.uint8), want.view(np.uint8)), f"{name} {mode}: differs from the oracle"
-    del outs, sends
-    torch.cuda.empty_cache()
+    check_every_element(I.WORKLOADS[name], "ring", modes=(mode,), label=f"{mode} ")
+    assert not E.protocol_status(), "a device-transport call was abandoned"
 
 
 def test_xwg_rejects_a_grid_that_cannot_be_resident():
@@ -215,9 +192,11 @@ def test_xwg_abandoned_call_is_reported_and_recovered(mode, monkeypatch):
     abandoned = False
     for attempt in range(5):
         announce(f"{mode} forced abandon, attempt {attempt}")
+        monkeypatch.setenv("EMU_DEBUG", "2")      # the library reads test hooks only in debug mode
         monkeypatch.setenv("EMU_XWG_SPIN_LIMIT", "0")
         E.allreduce_tensors(sends, recvs, "sum")
         monkeypatch.delenv("EMU_XWG_SPIN_LIMIT")
+        monkeypatch.delenv("EMU_DEBUG")
         torch.cuda.synchronize()
         for r in recvs:
             r.fill_(-7.0)

@@ -22,7 +22,7 @@ import sys
 HBM_PEAK_GBPS = 8000.0
 
 
-def main() -> int:
+def _main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--iters", type=int, default=20)
     args = ap.parse_args()
@@ -76,8 +76,15 @@ def main() -> int:
             print(f"[collbench] {coll:14s} {mode:8s} {t * 1e6:8.1f} us  {gbps:7.1f} GB/s", file=sys.stderr,
                   flush=True)
     print(json.dumps(out), flush=True)
-    E.comm_destroy()
     return 0
+
+
+def main() -> int:
+    from double_binary_tree_amd import emucomm as E
+    try:
+        return _main()
+    finally:
+        E.release()
 
 
 if __name__ == "__main__":

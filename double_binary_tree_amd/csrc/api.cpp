@@ -39,10 +39,23 @@ int xring_threads();
 int xring_slice_vectors(bool ll);
 int xring_capacity(bool ll, DType t, Op op, int cus);
 constexpr size_t kXMaxWorkspace = (size_t)4 << 30;       // per communicator and device
+// Defined in stream.hip.
+hipError_t launch_stream(int kind, const void* src, void* dst, uint64_t bytes, uint32_t key, int cus,
+                         hipStream_t s);
 
 namespace {
 
+// Tuning knobs and test hooks from the environment.  They are read only
+// when EMU_DEBUG is set (any value): without it every knob takes its
+// built-in value, so a deployment's behaviour never depends on stray
+// environment variables.
+bool debug_env() {
+  const char* v = std::getenv("EMU_DEBUG");
+  return v && *v;
+}
+
 long env_long(const char* name, long fallback) {
+  if (!debug_env()) return fallback;
   const char* v = std::getenv(name);
   if (!v || !*v) return fallback;
   char* end = nullptr;
@@ -52,6 +65,7 @@ long env_long(const char* name, long fallback) {
 
 // As env_long, but 0 is a valid value.
 long env_count(const char* name, long fallback) {
+  if (!debug_env()) return fallback;
   const char* v = std::getenv(name);
   if (!v || !*v) return fallback;
   char* end = nullptr;
@@ -59,33 +73,85 @@ long env_count(const char* name, long fallback) {
   return (end && *end == '\0' && x >= 0) ? x : fallback;
 }
 
+// Every device allocation of the library goes through these two, which
+// keep the count and size of what is live (emu_device_memory).
+size_t g_live_allocs = 0, g_live_bytes = 0;
+
+bool dev_alloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (hipMalloc(p, bytes) != hipSuccess) {
+    *p = nullptr;
+    return false;
+  }
+  ++g_live_allocs;
+  g_live_bytes += bytes;
+  return true;
+}
+
+void dev_free(void* p, size_t bytes) {
+  if (!p) return;
+  (void)hipFree(p);
+  --g_live_allocs;
+  g_live_bytes -= bytes;
+}
+
 struct DeviceBuffer {
   void* ptr = nullptr;
-  ~DeviceBuffer() { if (ptr) (void)hipFree(ptr); }
-  int upload(const void* src, size_t bytes) {
-    if (bytes == 0) return EMU_SUCCESS;
-    if (hipMalloc(&ptr, bytes) != hipSuccess) { ptr = nullptr; return EMU_ERR_HIP; }
-    if (hipMemcpy(ptr, src, bytes, hipMemcpyHostToDevice) != hipSuccess) return EMU_ERR_HIP;
+  size_t bytes = 0;
+  DeviceBuffer() = default;
+  DeviceBuffer(const DeviceBuffer&) = delete;
+  DeviceBuffer& operator=(const DeviceBuffer&) = delete;
+  ~DeviceBuffer() { dev_free(ptr, bytes); }
+  int alloc(size_t n) {
+    if (!dev_alloc(&ptr, n)) return EMU_ERR_HIP;
+    bytes = n;
+    return EMU_SUCCESS;
+  }
+  int upload(const void* src, size_t n) {
+    if (n == 0) return EMU_SUCCESS;
+    if (int e = alloc(n)) return e;
+    if (hipMemcpy(ptr, src, n, hipMemcpyHostToDevice) != hipSuccess) return EMU_ERR_HIP;
     return EMU_SUCCESS;
   }
 };
 
+// The tables a launch reads, by role.
+enum TableId : int { kTiles = 0, kRows, kTasks, kTable, kOrders, kXChan, kXSlices, kNumTables };
+
 struct Plan {
+  uint64_t serial = 0;        // unique per plan in the process
+  // Host copy of every table; the device copies are made from it on first
+  // use.
+  std::vector<unsigned char> host[kNumTables];
+  DeviceBuffer dev[kNumTables];
+  bool uploaded = false;
   // fused
-  DeviceBuffer tiles, rows;
   uint32_t ntiles = 0;
   int fused_grid = 0;
   // stepwise
-  DeviceBuffer tasks, table, orders;
   uint32_t ntasks = 0;
   int group = 0, block = 0, grid = 0;
   size_t lds = 0;
   uint32_t height = 0;
   bool ll = false;            // runs the LL-protocol kernels (one workgroup)
-  // stepwise ring across workgroups
+  // stepwise ring across workgroups: xchan = [nch][2] loop ranges then [nch]
+  // ring rows; xslices = slices per step, per loop
   bool xwg = false;
-  DeviceBuffer xchan, xslices;   // [nch][2] loop ranges then [nch] ring rows; [loops] slices per step
+
+  template <class T>
+  void keep(TableId id, const std::vector<T>& v) {
+    const unsigned char* b = reinterpret_cast<const unsigned char*>(v.data());
+    host[id].assign(b, b + v.size() * sizeof(T));
+  }
+  int upload() {
+    if (uploaded) return EMU_SUCCESS;
+    for (int i = 0; i < kNumTables; ++i)
+      if (int e = dev[i].upload(host[i].data(), host[i].size())) return e;
+    uploaded = true;
+    return EMU_SUCCESS;
+  }
 };
+uint64_t g_plan_serial = 0;
 
 // FIFOs and counters of the cross-workgroup ring, per communicator and
 // device: [fifo | tail counters | head counters | abandon word], all zero
@@ -113,22 +179,28 @@ struct Comm {
 };
 
 using CommKey = std::tuple<int, int, int, int, size_t, int, std::vector<int>>;
-std::map<CommKey, std::unique_ptr<Comm>> g_comms;   // built communicators, reused on re-init
+// The library's state lives on the heap and is never destroyed by the C++
+// runtime.  A static destructor would run at process exit, after the HIP
+// runtime (and any profiler attached to it) may already be torn down, and
+// the hipFree calls of the device tables from there can crash the exiting
+// process.  emu_comm_destroy releases everything; whatever is still held when
+// the process ends is reclaimed with the process.
+std::map<CommKey, std::unique_ptr<Comm>>& g_comms = *new std::map<CommKey, std::unique_ptr<Comm>>();
 Comm* g_active = nullptr;
 constexpr size_t kMaxCachedComms = 16;
 
-std::map<int, int> g_cu_count;
-std::map<int, size_t> g_lds_limit;
+std::map<int, int>& g_cu_count = *new std::map<int, int>();
+std::map<int, size_t>& g_lds_limit = *new std::map<int, size_t>();
 // Per device: the word an LL kernel sets when it abandons a call.
-std::map<int, uint32_t*> g_ll_status;
+std::map<int, uint32_t*>& g_ll_status = *new std::map<int, uint32_t*>();
 
 uint32_t* ll_status_word(int dev) {
   auto it = g_ll_status.find(dev);
   if (it != g_ll_status.end()) return it->second;
   void* p = nullptr;
-  if (hipMalloc(&p, sizeof(uint32_t)) != hipSuccess) return nullptr;
+  if (!dev_alloc(&p, sizeof(uint32_t))) return nullptr;
   if (hipMemset(p, 0, sizeof(uint32_t)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
-    (void)hipFree(p);
+    dev_free(p, sizeof(uint32_t));
     return nullptr;
   }
   g_ll_status[dev] = static_cast<uint32_t*>(p);
@@ -171,10 +243,7 @@ int xring_workspace(Comm& c, int dev, XWorkspace** out) {
   const uint64_t bytes = fifo_bytes + 2 * counter_bytes + 256;
   if (nslots > UINT32_MAX || bytes > kXMaxWorkspace) return EMU_ERR_INVALID_ARGUMENT;
   auto w = std::make_unique<XWorkspace>();
-  if (hipMalloc(&w->mem.ptr, bytes) != hipSuccess) {
-    w->mem.ptr = nullptr;
-    return EMU_ERR_HIP;
-  }
+  if (int e = w->mem.alloc(bytes)) return e;
   if (hipMemset(w->mem.ptr, 0, bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
   w->bytes = bytes;
   w->fifo_bytes = fifo_bytes;
@@ -223,10 +292,10 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     std::vector<uint32_t> chan = ring_channel_loops(c.topo, count, unit, chunk_count);
     if (chan.size() != 2u * c.nchannels || (c.nchannels && chan.back() != nloops)) return EMU_ERR_INTERNAL;
     for (const ChannelTopology& ch : c.topo.channels) chan.push_back((uint32_t)ch.ring_id);
-    if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
-    if (int e = p->orders.upload(orders.data(), orders.size() * sizeof(uint32_t))) return e;
-    if (int e = p->xchan.upload(chan.data(), chan.size() * sizeof(uint32_t))) return e;
-    if (int e = p->xslices.upload(slices.data(), slices.size() * sizeof(uint32_t))) return e;
+    p->keep(kTable, loops);
+    p->keep(kOrders, orders);
+    p->keep(kXChan, chan);
+    p->keep(kXSlices, slices);
     p->block = xring_threads();
     return EMU_SUCCESS;
   }
@@ -239,8 +308,8 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     else
       build_fused_coll_tiles(c.topo, coll, ord, count, unit, tile_elems, &tiles);
     p->ntiles = (uint32_t)tiles.size();
-    if (int e = p->tiles.upload(tiles.data(), tiles.size() * sizeof(Tile))) return e;
-    if (int e = p->rows.upload(ord.rows.data(), ord.rows.size() * sizeof(uint32_t))) return e;
+    p->keep(kTiles, tiles);
+    p->keep(kRows, ord.rows);
     const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 64);
     p->fused_grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntiles, (uint64_t)cus * per_cu));
     return EMU_SUCCESS;
@@ -280,9 +349,9 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     else
       build_ring_coll_tasks(c.topo, count, unit, chunk_count, slice_elems, &loops, &tasks, &orders);
     p->ntasks = (uint32_t)tasks.size();
-    if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(RingTask))) return e;
-    if (int e = p->table.upload(loops.data(), loops.size() * sizeof(RingLoopBlock))) return e;
-    if (int e = p->orders.upload(orders.data(), orders.size() * sizeof(uint32_t))) return e;
+    p->keep(kTasks, tasks);
+    p->keep(kTable, loops);
+    p->keep(kOrders, orders);
   } else {
     // One pipeline per resident workgroup (tasks per CU = occupancy, or the
     // tuning override EMU_TREE_TASKS_PER_CU).
@@ -296,8 +365,8 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     uint32_t h = 0;
     for (const auto& ch : c.topo.channels) h = std::max<uint32_t>(h, (uint32_t)ch.height);
     p->height = h;
-    if (int e = p->tasks.upload(tasks.data(), tasks.size() * sizeof(TreeTask))) return e;
-    if (int e = p->table.upload(nodes.data(), nodes.size() * sizeof(TreeNode))) return e;
+    p->keep(kTasks, tasks);
+    p->keep(kTable, nodes);
   }
   const int occ = p->ll ? ll_occupancy(ring, t, op, p->block, p->lds)
                         : stepwise_occupancy(ring, t, op, p->block, p->lds, p->group);
@@ -407,12 +476,18 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
 namespace emu {
 namespace {
 
-// Shared by the three collectives: argument checks (before anything is
-// enqueued), plan lookup, launch.  Rank r's send buffer holds send_elems
-// elements and its receive buffer recv_elems; `count` is the all-reduce
-// count or the block size.  In place means recvbufs[r] == sendbufs[r] +
-// inplace_off elements (0 for the all-reduce, r*count for reduce-scatter);
-// for all-gather, sendbufs[r] == recvbufs[r] + r*count.
+// Device addresses of the tables one launch reads.
+struct Tables {
+  const void* t[kNumTables] = {};
+  uint32_t* status = nullptr;   // LL / device-transport abandon word
+};
+
+// Shared by the collectives: argument checks (before anything is enqueued),
+// plan lookup, launch.  Rank r's send buffer holds send_elems elements and
+// its receive buffer recv_elems; `count` is the all-reduce count or the
+// block size.  In place means recvbufs[r] == sendbufs[r] + inplace_off
+// elements (0 for the all-reduce, r*count for reduce-scatter); for
+// all-gather, sendbufs[r] == recvbufs[r] + r*count.
 int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype,
                    int op, void* stream) {
   Comm* c = g_active;
@@ -465,11 +540,19 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
   auto it = c->plans.find(key);
   if (it == c->plans.end()) {
     auto p = std::make_unique<Plan>();
+    p->serial = ++g_plan_serial;
     if (int e = make_plan(*c, coll, algo, dev, count, t, o, p.get())) return e;
     it = c->plans.emplace(key, std::move(p)).first;
   }
-  const Plan& p = *it->second;
+  Plan& p = *it->second;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  Tables tb;
+  if (int e = p.upload()) return e;
+  for (int i = 0; i < kNumTables; ++i) tb.t[i] = p.dev[i].ptr;
+  if (p.ll || p.xwg) {
+    tb.status = ll_status_word(dev);
+    if (!tb.status) return EMU_ERR_HIP;
+  }
   hipError_t err;
   if (c->fused) {
     FusedArgs a{};
@@ -486,17 +569,17 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     // Each XCD takes a contiguous run of tiles from 12 ranks up.  Measured
     // on MI355X (fused, full-size workloads): 15, 16 and 32 ranks gain up to
     // 20% with buffers where torch places them and stay within 2% with the
-    // staggered layout; 8 ranks lose 4-8% either way.  Tuning override
+    // staggered layout; 8 ranks lose 4-8% either way.  Debug knob
     // EMU_FUSED_XCD_RUNS: 1 off, 2 on.
     a.xcd_runs = env_long("EMU_FUSED_XCD_RUNS", n >= 12 ? 2 : 1) == 2 ? 1 : 0;
-    err = launch_fused(coll, t, o, ord.mode, a, static_cast<const Tile*>(p.tiles.ptr),
-                       static_cast<const uint32_t*>(p.rows.ptr), p.fused_grid, s);
+    err = launch_fused(coll, t, o, ord.mode, a, static_cast<const Tile*>(tb.t[kTiles]),
+                       static_cast<const uint32_t*>(tb.t[kRows]), p.fused_grid, s);
   } else {
     StepArgs a{};
     for (int r = 0; r < n; ++r) { a.send[r] = sendbufs[r]; a.recv[r] = recvbufs[r]; }
-    a.tasks = p.tasks.ptr;
-    a.table = p.table.ptr;
-    a.orders = static_cast<const uint32_t*>(p.orders.ptr);
+    a.tasks = tb.t[kTasks];
+    a.table = tb.t[kTable];
+    a.orders = static_cast<const uint32_t*>(tb.t[kOrders]);
     a.count = count;
     a.block = count;
     a.ntasks = p.ntasks;
@@ -504,33 +587,29 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
     a.group = (uint32_t)p.group;
     a.height = p.height;
     if (p.xwg) {
-      uint32_t* status = ll_status_word(dev);
-      if (!status) return EMU_ERR_HIP;
       const XWorkspace& w = *c->xws.at(dev);
       char* base = static_cast<char*>(w.mem.ptr);
-      const uint32_t* chan = static_cast<const uint32_t*>(p.xchan.ptr);
+      const uint32_t* chan = static_cast<const uint32_t*>(tb.t[kXChan]);
       XArgs x{};
       x.chan_loops = chan;
       x.chan_ring = chan + 2 * c->nchannels;
-      x.loop_slices = static_cast<const uint32_t*>(p.xslices.ptr);
+      x.loop_slices = static_cast<const uint32_t*>(tb.t[kXSlices]);
       x.fifo = base;
       x.tail = reinterpret_cast<uint32_t*>(base + w.fifo_bytes);
       x.head = reinterpret_cast<uint32_t*>(base + w.fifo_bytes + w.counter_bytes);
       x.abandon = reinterpret_cast<uint32_t*>(base + w.fifo_bytes + 2 * w.counter_bytes);
-      x.status = status;
+      x.status = tb.status;
       x.nslots = w.nslots;
-      // polls before a wait is abandoned; EMU_XWG_SPIN_LIMIT lowers it so
-      // that tests can force the abandon path from the host
+      // polls before a wait is abandoned; the debug hook EMU_XWG_SPIN_LIMIT
+      // lowers it so that tests can force the abandon path from the host
       x.spin_limit = (uint32_t)env_count("EMU_XWG_SPIN_LIMIT", 1L << 22);
-      err = launch_xring(c->ll, t, o, a, x, static_cast<const RingLoopBlock*>(p.table.ptr),
-                         static_cast<const uint32_t*>(p.orders.ptr), p.grid, s);
+      err = launch_xring(c->ll, t, o, a, x, static_cast<const RingLoopBlock*>(tb.t[kTable]),
+                         static_cast<const uint32_t*>(tb.t[kOrders]), p.grid, s);
     } else if (p.ll) {
-      uint32_t* status = ll_status_word(dev);
-      if (!status) return EMU_ERR_HIP;
-      // polls before a wait is abandoned; EMU_LL_SPIN_LIMIT lowers it so
-      // that tests can force the abandon path from the host
+      // polls before a wait is abandoned; the debug hook EMU_LL_SPIN_LIMIT
+      // lowers it so that tests can force the abandon path from the host
       const uint32_t spin = (uint32_t)env_count("EMU_LL_SPIN_LIMIT", 1L << 22);
-      err = launch_ll(algo == Algo::Ring, t, o, a, status, spin, p.grid, p.block, p.lds, s);
+      err = launch_ll(algo == Algo::Ring, t, o, a, tb.status, spin, p.grid, p.block, p.lds, s);
     } else {
       err = launch_stepwise(coll, algo == Algo::Ring, t, o, a, p.grid, p.block, p.lds, s);
     }
@@ -614,8 +693,15 @@ int emu_comm_destroy(void) {
   if (has_plans) (void)hipDeviceSynchronize();
   g_active = nullptr;
   g_comms.clear();
-  for (auto& kv : g_ll_status) (void)hipFree(kv.second);
+  for (auto& kv : g_ll_status) dev_free(kv.second, sizeof(uint32_t));
   g_ll_status.clear();
+  return EMU_SUCCESS;
+}
+
+int emu_device_memory(size_t* allocations, size_t* bytes) {
+  if (!allocations || !bytes) return EMU_ERR_INVALID_ARGUMENT;
+  *allocations = g_live_allocs;
+  *bytes = g_live_bytes;
   return EMU_SUCCESS;
 }
 
@@ -637,13 +723,13 @@ int emu_protocol_status(int* abandoned) {
   if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
   auto it = g_ll_status.find(dev);
   if (it == g_ll_status.end()) return EMU_SUCCESS;
-  uint32_t v = 0;
   if (hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
+  uint32_t v = 0;
   if (hipMemcpy(&v, it->second, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return EMU_ERR_HIP;
+  if (v && hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess) return EMU_ERR_HIP;
   if (v) {
     // An abandoned cross-workgroup call leaves its FIFO counters mismatched:
     // clear every such workspace on the device with the status word.
-    if (hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess) return EMU_ERR_HIP;
     for (const auto& kv : g_comms) {
       auto w = kv.second->xws.find(dev);
       if (w != kv.second->xws.end() && hipMemset(w->second->mem.ptr, 0, w->second->bytes) != hipSuccess)
@@ -653,6 +739,25 @@ int emu_protocol_status(int* abandoned) {
   }
   *abandoned = v ? 1 : 0;
   return EMU_SUCCESS;
+}
+
+int emu_stream_probe(int kind, const void* src, void* dst, size_t bytes, void* stream) {
+  if (kind != EMU_STREAM_READ && kind != EMU_STREAM_WRITE && kind != EMU_STREAM_COPY) return EMU_ERR_INVALID_ARGUMENT;
+  if (bytes % kVecBytes) return EMU_ERR_INVALID_ARGUMENT;
+  const bool reads = kind != EMU_STREAM_WRITE;
+  if (!dst || (uintptr_t)dst % kVecBytes) return EMU_ERR_INVALID_ARGUMENT;
+  if (reads && (!src || (uintptr_t)src % kVecBytes)) return EMU_ERR_INVALID_ARGUMENT;
+  if (kind == EMU_STREAM_COPY) {
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+    if (a < b + bytes && b < a + bytes) return EMU_ERR_INVALID_ARGUMENT;
+  }
+  if (bytes == 0) return EMU_SUCCESS;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
+  const uint32_t key = 0x9E3779B9u ^ (uint32_t)(bytes >> 4);
+  return launch_stream(kind, src, dst, bytes, key, cu_count(dev), static_cast<hipStream_t>(stream)) == hipSuccess
+             ? EMU_SUCCESS
+             : EMU_ERR_HIP;
 }
 
 const char* emu_strerror(int code) {

@@ -75,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.emu_buffer_layout.restype = ctypes.c_int
         L.emu_protocol_status.argtypes = [ctypes.POINTER(ctypes.c_int)]
         L.emu_protocol_status.restype = ctypes.c_int
+        L.emu_device_memory.argtypes = [ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.emu_device_memory.restype = ctypes.c_int
+        L.emu_stream_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+        L.emu_stream_probe.restype = ctypes.c_int
         L.emu_strerror.argtypes = [ctypes.c_int]
         L.emu_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -222,6 +227,31 @@ def protocol_status() -> bool:
 
 def comm_destroy() -> None:
     _check(lib().emu_comm_destroy(), "emu_comm_destroy")
+
+
+STREAM = {"read": 0, "write": 1, "copy": 2}
+
+
+def stream_probe(kind: str, src: int, dst: int, nbytes: int, stream: int = 0) -> None:
+    """emu_stream_probe: one pass of the read-only, write-only or copy
+    streaming kernel (pointers as integers)."""
+    _check(lib().emu_stream_probe(STREAM[kind], ctypes.c_void_p(int(src)), ctypes.c_void_p(int(dst)), nbytes,
+                                  ctypes.c_void_p(int(stream))), "emu_stream_probe")
+
+
+def release() -> None:
+    """emu_comm_destroy if the library was loaded: frees its device memory
+    while the HIP runtime is still up.  Scripts call it before they return."""
+    if _lib is not None:
+        comm_destroy()
+
+
+def device_memory() -> tuple[int, int]:
+    """(allocations, bytes) of device memory the library holds now."""
+    n = ctypes.c_size_t(0)
+    b = ctypes.c_size_t(0)
+    _check(lib().emu_device_memory(ctypes.byref(n), ctypes.byref(b)), "emu_device_memory")
+    return int(n.value), int(b.value)
 
 
 # --- torch convenience (device memory and streams only) ---------------------

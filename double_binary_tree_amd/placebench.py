@@ -20,7 +20,7 @@ MODES = ("fused", "stepwise")
 ITERS = 20
 
 
-def main() -> int:
+def _main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None)
     args = ap.parse_args()
@@ -102,6 +102,14 @@ def main() -> int:
         with open(args.out, "w", encoding="utf-8") as f:
             f.writelines(lines)
     return 0
+
+
+def main() -> int:
+    from double_binary_tree_amd import emucomm as E
+    try:
+        return _main()
+    finally:
+        E.release()
 
 
 if __name__ == "__main__":

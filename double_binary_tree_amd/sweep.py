@@ -65,7 +65,7 @@ def intervals(rows, key_a, key_b):
     return out
 
 
-def main() -> int:
+def _main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--max-pow", type=int, default=26, help="largest count = 2**max_pow elements")
     ap.add_argument("--min-pow", type=int, default=1)
@@ -147,6 +147,14 @@ def write_report(path, rows):
         lines.append("\n")
     with open(path, "w", encoding="utf-8") as f:
         f.writelines(lines)
+
+
+def main() -> int:
+    from double_binary_tree_amd import emucomm as E
+    try:
+        return _main()
+    finally:
+        E.release()
 
 
 if __name__ == "__main__":

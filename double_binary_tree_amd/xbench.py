@@ -53,7 +53,7 @@ def time_graph(E, sptr, rptr, count, torch, replays: int) -> float:
     return a.elapsed_time(b) * 1e3 / (replays * GRAPH_LAUNCHES)
 
 
-def main() -> int:
+def _main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None)
     ap.add_argument("--quick", action="store_true", help="full size at 32 channels only")
@@ -115,6 +115,14 @@ def main() -> int:
         with open(args.out, "w", encoding="utf-8") as f:
             f.writelines(lines)
     return 0
+
+
+def main() -> int:
+    from double_binary_tree_amd import emucomm as E
+    try:
+        return _main()
+    finally:
+        E.release()
 
 
 if __name__ == "__main__":

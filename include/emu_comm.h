@@ -125,6 +125,14 @@ extern "C" {
 #define EMU_MAX_RANKS 64
 #define EMU_MAX_CHANNELS 64
 
+/* Environment.  The library reads no environment variable unless EMU_DEBUG
+ * is set.  With EMU_DEBUG set, tuning knobs (EMU_FUSED_BLOCKS_PER_CU,
+ * EMU_FUSED_XCD_RUNS, EMU_TREE_TASKS_PER_CU, EMU_STEP_GROUP, EMU_XWG_SLOTS)
+ * and test hooks that shorten the bounded waits (EMU_LL_SPIN_LIMIT,
+ * EMU_XWG_SPIN_LIMIT) override the built-in values of plans built after
+ * they are set; EMU_DEBUG=1 also prints every tree record at init.  They
+ * are for debugging and measurement only. */
+
 /*
  * emu_comm_init - build the communicator: per-channel tree records for
  * `nranks` virtual ranks on `nnodes` nodes (ranks are node-major:
@@ -300,10 +308,21 @@ int emu_tree_depth(int* depth);
 
 /*
  * emu_comm_destroy - free the communicator and every device resource the
- * library allocated.  Call with no work of the library pending on any
- * stream.  Destroying when nothing is initialised succeeds.
+ * library allocated (tables, FIFO workspaces, protocol status words).  Call
+ * with no work of the library pending on any stream.  Destroying when
+ * nothing is initialised succeeds.  Nothing is freed at process exit: what
+ * a process still holds when it ends is reclaimed with the process (freeing
+ * from exit-time destructors would race the HIP runtime's own teardown).
  */
 int emu_comm_destroy(void);
+
+/*
+ * emu_device_memory - how many device allocations the library holds now,
+ * and their total size in bytes (tables, FIFO workspaces, status words; not
+ * the caller's buffers).  Zero after emu_comm_destroy.  Host only.
+ * Errors: EMU_ERR_INVALID_ARGUMENT for a NULL pointer.
+ */
+int emu_device_memory(size_t* allocations, size_t* bytes);
 
 /*
  * emu_protocol_status - whether an LL or EMU_TRANSPORT_DEVICE all-reduce on
@@ -334,6 +353,27 @@ int emu_protocol_status(int* abandoned);
  * pool size that does not fit in size_t.
  */
 int emu_buffer_layout(size_t nbufs, size_t bytes, size_t offsets[], size_t* pool_bytes);
+
+/*
+ * emu_stream_probe - enqueue one pass of a 128-bit streaming kernel on
+ * `stream`, for measurement: the same-run HBM rates that the collectives'
+ * bandwidth is compared with (a copy of the same byte count is the pages'
+ * usual yardstick; an all-reduce moves half reads and half writes, so its
+ * practical ceiling lies between the read-only and write-only rates).
+ * Whole 16-byte vectors, non-temporal, as the collectives access memory.
+ *   kind   EMU_STREAM_READ: read `bytes` at src (dst: 16 bytes the kernel
+ *          may write, practically never);  EMU_STREAM_WRITE: write `bytes`
+ *          of a fixed pattern at dst (src unused);  EMU_STREAM_COPY: copy
+ *          `bytes` from src to dst (no overlap)
+ *   bytes  a multiple of 16; 0 is a no-op.  Pointers 16-byte aligned.
+ * Errors: EMU_ERR_INVALID_ARGUMENT (unknown kind, NULL or misaligned
+ * pointer, bytes not a multiple of 16, overlapping copy); EMU_ERR_HIP for
+ * a launch failure.  Needs no communicator.
+ */
+#define EMU_STREAM_READ 0
+#define EMU_STREAM_WRITE 1
+#define EMU_STREAM_COPY 2
+int emu_stream_probe(int kind, const void* src, void* dst, size_t bytes, void* stream);
 
 /* emu_strerror - static description of a result code (never NULL). */
 const char* emu_strerror(int code);

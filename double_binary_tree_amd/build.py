@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libemucomm.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["fused.hip", "stepwise.hip", "ll.hip", "xwg.hip", "stream.hip"]
+HIP_SOURCES = ["fused.hip", "stepwise.hip", "ll.hip", "xwg.hip", "noalloc.hip", "stream.hip"]
 CXX_SOURCES = ["api.cpp", "plan.cpp", "topology.cpp"]
 
 HIPCC_FLAGS = [

@@ -39,6 +39,11 @@ int xring_threads();
 int xring_slice_vectors(bool ll);
 int xring_capacity(bool ll, DType t, Op op, int cus);
 constexpr size_t kXMaxWorkspace = (size_t)4 << 30;       // per communicator and device
+// Defined in noalloc.hip: the static scratch array of the no-allocation
+// entry point, its size, and its address on a device (looked up once per
+// device; with create == false only reported if already looked up).
+hipError_t scratch_address(int dev, bool create, void** out);
+size_t scratch_bytes();
 // Defined in stream.hip.
 hipError_t launch_stream(int kind, const void* src, void* dst, uint64_t bytes, uint32_t key, int cus,
                          hipStream_t s);
@@ -120,8 +125,9 @@ enum TableId : int { kTiles = 0, kRows, kTasks, kTable, kOrders, kXChan, kXSlice
 
 struct Plan {
   uint64_t serial = 0;        // unique per plan in the process
-  // Host copy of every table; the device copies are made from it on first
-  // use.
+  // Host copy of every table (the no-allocation entry point copies them into
+  // its static scratch); device copies are made on first use by the
+  // allocating entry points.
   std::vector<unsigned char> host[kNumTables];
   DeviceBuffer dev[kNumTables];
   bool uploaded = false;
@@ -476,23 +482,60 @@ int emu_comm_init(int nranks, int nnodes, int algo, int nchannels, size_t chunk_
 namespace emu {
 namespace {
 
+// The no-allocation entry point keeps its tables in a static device array
+// (noalloc.hip), one per device: [status word | tables, each 256-byte
+// aligned].  Per device, the serial of the plan whose tables it holds.
+constexpr size_t kScratchAlign = 256;
+std::map<int, uint64_t>& g_scratch_serial = *new std::map<int, uint64_t>();
+
 // Device addresses of the tables one launch reads.
 struct Tables {
   const void* t[kNumTables] = {};
   uint32_t* status = nullptr;   // LL / device-transport abandon word
 };
 
+// Points `tb` at the plan's tables in the scratch array of `dev`, copying
+// them there (stream-ordered on `s`) unless the array already holds them.
+int stage_scratch(const Plan& p, int dev, hipStream_t s, Tables* tb) {
+  void* base = nullptr;
+  if (scratch_address(dev, true, &base) != hipSuccess || !base) return EMU_ERR_HIP;
+  size_t off[kNumTables];
+  size_t end = kScratchAlign;   // the status word sits at offset 0
+  for (int i = 0; i < kNumTables; ++i) {
+    off[i] = end;
+    end += (p.host[i].size() + kScratchAlign - 1) / kScratchAlign * kScratchAlign;
+  }
+  if (end > scratch_bytes()) return EMU_ERR_INVALID_ARGUMENT;
+  unsigned char* b = static_cast<unsigned char*>(base);
+  auto it = g_scratch_serial.find(dev);
+  if (it == g_scratch_serial.end() || it->second != p.serial) {
+    g_scratch_serial[dev] = 0;   // no plan until every copy is enqueued
+    for (int i = 0; i < kNumTables; ++i) {
+      if (p.host[i].empty()) continue;
+      if (hipMemcpyAsync(b + off[i], p.host[i].data(), p.host[i].size(), hipMemcpyHostToDevice, s) != hipSuccess)
+        return EMU_ERR_HIP;
+    }
+    g_scratch_serial[dev] = p.serial;
+  }
+  for (int i = 0; i < kNumTables; ++i) tb->t[i] = p.host[i].empty() ? nullptr : b + off[i];
+  tb->status = reinterpret_cast<uint32_t*>(b);
+  return EMU_SUCCESS;
+}
+
 // Shared by the collectives: argument checks (before anything is enqueued),
 // plan lookup, launch.  Rank r's send buffer holds send_elems elements and
 // its receive buffer recv_elems; `count` is the all-reduce count or the
 // block size.  In place means recvbufs[r] == sendbufs[r] + inplace_off
 // elements (0 for the all-reduce, r*count for reduce-scatter); for
-// all-gather, sendbufs[r] == recvbufs[r] + r*count.
+// all-gather, sendbufs[r] == recvbufs[r] + r*count.  `noalloc`: the tables
+// go to the static scratch array and nothing is allocated on the device.
 int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype,
-                   int op, void* stream) {
+                   int op, void* stream, bool noalloc = false) {
   Comm* c = g_active;
   if (!c) return EMU_ERR_NOT_INITIALIZED;
   if (!valid_dtype(dtype) || !valid_op(op) || !sendbufs || !recvbufs) return EMU_ERR_INVALID_ARGUMENT;
+  // the device transport's FIFOs are far larger than the scratch array
+  if (noalloc && c->xwg) return EMU_ERR_INVALID_ARGUMENT;
   const DType t = static_cast<DType>(dtype);
   const Op o = static_cast<Op>(op);
   const int n = c->nranks;
@@ -547,11 +590,15 @@ int run_collective(Coll coll, const void* const sendbufs[], void* const recvbufs
   Plan& p = *it->second;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Tables tb;
-  if (int e = p.upload()) return e;
-  for (int i = 0; i < kNumTables; ++i) tb.t[i] = p.dev[i].ptr;
-  if (p.ll || p.xwg) {
-    tb.status = ll_status_word(dev);
-    if (!tb.status) return EMU_ERR_HIP;
+  if (noalloc) {
+    if (int e = stage_scratch(p, dev, s, &tb)) return e;
+  } else {
+    if (int e = p.upload()) return e;
+    for (int i = 0; i < kNumTables; ++i) tb.t[i] = p.dev[i].ptr;
+    if (p.ll || p.xwg) {
+      tb.status = ll_status_word(dev);
+      if (!tb.status) return EMU_ERR_HIP;
+    }
   }
   hipError_t err;
   if (c->fused) {
@@ -625,6 +672,11 @@ extern "C" {
 int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype, int op,
                   void* stream) {
   return run_collective(kAllReduce, sendbufs, recvbufs, count, dtype, op, stream);
+}
+
+int emu_allreduce_noalloc(const void* const sendbufs[], void* const recvbufs[], size_t count, int dtype, int op,
+                          void* stream) {
+  return run_collective(kAllReduce, sendbufs, recvbufs, count, dtype, op, stream, true);
 }
 
 int emu_reduce_scatter(const void* const sendbufs[], void* const recvbufs[], size_t recvcount, int dtype, int op,
@@ -722,11 +774,22 @@ int emu_protocol_status(int* abandoned) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return EMU_ERR_HIP;
   auto it = g_ll_status.find(dev);
-  if (it == g_ll_status.end()) return EMU_SUCCESS;
+  void* scratch = nullptr;
+  (void)scratch_address(dev, false, &scratch);
+  if (it == g_ll_status.end() && !scratch) return EMU_SUCCESS;
   if (hipDeviceSynchronize() != hipSuccess) return EMU_ERR_HIP;
   uint32_t v = 0;
-  if (hipMemcpy(&v, it->second, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return EMU_ERR_HIP;
-  if (v && hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess) return EMU_ERR_HIP;
+  if (scratch) {
+    // the no-allocation entry point's LL calls report in the scratch array
+    if (hipMemcpy(&v, scratch, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return EMU_ERR_HIP;
+    if (v && hipMemset(scratch, 0, sizeof(uint32_t)) != hipSuccess) return EMU_ERR_HIP;
+  }
+  if (it != g_ll_status.end()) {
+    uint32_t w = 0;
+    if (hipMemcpy(&w, it->second, sizeof(w), hipMemcpyDeviceToHost) != hipSuccess) return EMU_ERR_HIP;
+    if (w && hipMemset(it->second, 0, sizeof(uint32_t)) != hipSuccess) return EMU_ERR_HIP;
+    v |= w;
+  }
   if (v) {
     // An abandoned cross-workgroup call leaves its FIFO counters mismatched:
     // clear every such workspace on the device with the status word.

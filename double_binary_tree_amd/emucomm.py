@@ -51,6 +51,9 @@ def lib() -> ctypes.CDLL:
         L.emu_allreduce.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                     ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.emu_allreduce.restype = ctypes.c_int
+        L.emu_allreduce_noalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.emu_allreduce_noalloc.restype = ctypes.c_int
         L.emu_reduce_scatter.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
                                          ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.emu_reduce_scatter.restype = ctypes.c_int
@@ -141,6 +144,16 @@ def allreduce_raw(sendptrs, recvptrs, count: int, dtype: int, op: int, stream: i
 
 def allreduce(sendptrs, recvptrs, count: int, dtype: str, op: str, stream: int = 0) -> None:
     _check(allreduce_raw(sendptrs, recvptrs, count, DTYPE[dtype], OP[op], stream), "emu_allreduce")
+
+
+def allreduce_noalloc_raw(sendptrs, recvptrs, count: int, dtype: int, op: int, stream: int = 0) -> int:
+    return lib().emu_allreduce_noalloc(_ptrs(sendptrs), _ptrs(recvptrs), count, dtype, op,
+                                       ctypes.c_void_p(int(stream)))
+
+
+def allreduce_noalloc(sendptrs, recvptrs, count: int, dtype: str, op: str, stream: int = 0) -> None:
+    _check(allreduce_noalloc_raw(sendptrs, recvptrs, count, DTYPE[dtype], OP[op], stream),
+           "emu_allreduce_noalloc")
 
 
 def _ptrs(ptrs):

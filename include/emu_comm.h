@@ -218,6 +218,33 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
                   int dtype, int op, void* stream);
 
 /*
+ * emu_allreduce_noalloc - emu_allreduce for callers that cannot allocate
+ * device memory: code under HIP stream capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, results (bit for bit)
+ * and errors as emu_allreduce.  It never calls hipMalloc, hipFree or any
+ * allocating library routine: instead of tables in device buffers the
+ * library allocates, it keeps the call's tables (and the LL status word) in
+ * a static device array of EMU_NOALLOC_SCRATCH_BYTES bytes that every GPU
+ * the library runs on holds from module load until the process ends.  Its
+ * device address is looked up once per device, on the first call there.
+ * A call copies its tables into the array with hipMemcpyAsync on `stream`
+ * (skipped when the array already holds the same plan's tables), so the
+ * caller passes only inputs and outputs.  Host memory for a new shape's
+ * tables is taken on its first call and kept with the communicator.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * tables: calls on one GPU that overlap in time (on different streams, or
+ * from several threads) race; order them, e.g. on one stream.  Modes: fused
+ * and stepwise (SIMPLE or LL; an LL abandon is reported by
+ * emu_protocol_status).  Additional errors: EMU_ERR_INVALID_ARGUMENT for an
+ * EMU_TRANSPORT_DEVICE communicator (its FIFOs are far larger than the
+ * array) and for a call whose tables exceed the array (from about 1 GiB per
+ * rank in fused mode; the stepwise tables are much smaller).
+ */
+#define EMU_NOALLOC_SCRATCH_BYTES (4u << 20)
+int emu_allreduce_noalloc(const void* const sendbufs[], void* const recvbufs[], size_t count,
+                          int dtype, int op, void* stream);
+
+/*
  * emu_reduce_scatter - enqueue one reduce-scatter on `stream`: the first
  * half of the ring all-reduce run on its own (page "all-reduce 每张卡要发多少
  * 数据? ring 和 tree 有什么区别?", section "先弄清楚:每个概念是什么" and

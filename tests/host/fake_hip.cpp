@@ -3,7 +3,8 @@
 // resource handling can be checked on a machine without a GPU.
 //
 // "Device" allocations are host memory, tracked one by one: a free of an
-// unknown pointer, a copy or fill that leaves a live allocation, or a table pointer handed to a launcher outside
+// unknown pointer, a copy or fill that leaves a live allocation (or the
+// static scratch array), or a table pointer handed to a launcher outside
 // live memory aborts with a message.  Launchers copy the tables they
 // receive, so that a driver can compare what two entry points pass.
 #include <hip/hip_runtime_api.h>
@@ -26,6 +27,8 @@ std::map<const unsigned char*, size_t>& live() {
   return *m;
 }
 
+alignas(256) unsigned char g_scratch[EMU_NOALLOC_SCRATCH_BYTES];
+bool g_scratch_seen = false;
 size_t g_mallocs = 0;
 
 [[noreturn]] void fail(const std::string& what) {
@@ -33,9 +36,10 @@ size_t g_mallocs = 0;
   std::abort();
 }
 
-// True if [p, p + n) lies inside one live allocation.
+// True if [p, p + n) lies inside one live allocation or the scratch array.
 bool in_device_memory(const void* p, size_t n) {
   const unsigned char* q = static_cast<const unsigned char*>(p);
+  if (q >= g_scratch && q + n <= g_scratch + sizeof(g_scratch)) return g_scratch_seen;
   auto it = live().upper_bound(q);
   if (it == live().begin()) return false;
   --it;
@@ -168,6 +172,15 @@ hipError_t launch_xring(bool, DType, Op, const StepArgs&, const XArgs& x, const 
 int xring_threads() { return 256; }
 int xring_slice_vectors(bool ll) { return 256 * (ll ? 2 : 8); }
 int xring_capacity(bool, DType, Op, int cus) { return 2 * cus; }
+
+hipError_t scratch_address(int, bool create, void** out) {
+  *out = nullptr;
+  if (!g_scratch_seen && !create) return hipSuccess;
+  g_scratch_seen = true;
+  *out = g_scratch;
+  return hipSuccess;
+}
+size_t scratch_bytes() { return sizeof(g_scratch); }
 
 hipError_t launch_stream(int kind, const void* src, void* dst, uint64_t bytes, uint32_t, int, hipStream_t) {
   if (kind != EMU_STREAM_WRITE) require(src, bytes, "stream source");

@@ -5,8 +5,10 @@ under AddressSanitizer and UndefinedBehaviorSanitizer against a host-only
 stand-in for the HIP runtime and the kernel launchers
 (tests/host/fake_hip.cpp), which tracks every device allocation and checks
 every table pointer a launch receives.  It checks that emu_comm_destroy
-frees every device allocation (tables, FIFO workspaces, LL status words)
-and that dropping cached communicators frees theirs."""
+frees every device allocation (tables, FIFO workspaces, LL status words),
+that dropping cached communicators frees theirs, that
+emu_allreduce_noalloc never allocates and hands its kernels the same tables
+as emu_allreduce (across shape changes), and what it refuses."""
 
 import os
 import shutil

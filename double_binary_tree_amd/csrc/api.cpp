@@ -329,8 +329,10 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
   // Lanes per virtual rank: the widest group that fits one workgroup
   // (N*G <= 1024 threads) and the device's LDS per workgroup.
   const size_t lds_limit = lds_per_block(dev);
-  p->group = p->ll ? 64 : (int)env_long("EMU_STEP_GROUP", 64);   // tuning override; must be a power of two
-  if (p->group > 64 || (p->group & (p->group - 1))) p->group = 64;
+  // Lanes per rank: 64, 32 or 16 (one, two or four ranks per wave; 64 ranks
+  // in 1024 threads need 16).  Debug knob EMU_STEP_GROUP.
+  p->group = p->ll ? 64 : (int)env_long("EMU_STEP_GROUP", 64);
+  if (p->group > 64 || p->group < 16 || (p->group & (p->group - 1))) p->group = 64;
   // LDS: ring 2 parities of slots plus 2 x N staged block descriptors and
   // 2 staged ring orders, tree 2 parities x (up, down) slots.
   auto lds_of = [&](int g) {
@@ -338,7 +340,7 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     return (ring ? 2u : 4u) * (size_t)n * g * vpl * kVecBytes +
            (ring ? 2u * n * sizeof(RingLoopBlock) + 2u * kMaxRanks : 0u);
   };
-  while (!p->ll && p->group > 4 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
+  while (!p->ll && p->group > 16 && (n * p->group > 1024 || lds_of(p->group) > lds_limit)) p->group /= 2;
   if (n * p->group > 1024 || lds_of(p->group) > lds_limit) return EMU_ERR_INTERNAL;
   p->block = (n * p->group + 63) / 64 * 64;
   const uint64_t slice_elems = (uint64_t)p->group * vpl * unit;

@@ -148,6 +148,13 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     const RingLoopBlock* blk = desc + set * n;
     // the rank at position r
     const uint32_t me = active ? wave_u32<WAVE>(order[set * kMaxRanks + r]) : 0;
+    // Its buffers, looked up once per task.  With G < 64 the rank differs
+    // between the lanes of a wave, and indexing the argument's pointer table
+    // with it is a vector load whose wait (vmcnt 0) would also wait for
+    // every prefetch in flight; read here, that wait happens once per task
+    // instead of at every step.
+    const char* const src_me = static_cast<const char*>(a.send[me]);
+    char* const dst_me = static_cast<char*>(a.recv[me]);
     // byte distance between a block's place and the rank's own buffer
     const uint64_t my_shift = COLL == kAllReduce ? 0 : (uint64_t)me * a.block * ESZ;
     const uint64_t load_shift = COLL == kAllGather ? my_shift : 0;
@@ -180,9 +187,9 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     // when it is consumed (fix_block).
     auto load_block = [&](uint32_t b, u32x4 (&x)[V], bool enable) {
       const View w = view_of(b);
-      const void* src = a.send[me];
+      const char* const src = src_me;
       if constexpr (WAVE) {
-        const auto rs = buffer_view(static_cast<const char*>(src) + (w.cell * ESZ - load_shift));
+        const auto rs = buffer_view(src + (w.cell * ESZ - load_shift));
         if (enable && whole(w)) {
 #pragma unroll
           for (int v = 0; v < V; ++v) x[v] = ld_buf(rs, (uint32_t)((v * g + p) * kVecBytes));
@@ -210,13 +217,13 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
         for (int v = 0; v < V; ++v) {
           const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
           const int nb = nbytes_of(w, pos);
-          if (nb > 0 && nb < kVecBytes) x[v] = ld_part(a.send[me], pos * ESZ - load_shift, nb);
+          if (nb > 0 && nb < kVecBytes) x[v] = ld_part(src_me, pos * ESZ - load_shift, nb);
         }
       }
     };
     auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
       const View w = view_of(b);
-      void* dst = a.recv[me];
+      char* const dst = dst_me;
       if (whole(w)) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
@@ -318,21 +325,44 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
 
 // ---------------------------------------------------------------------------
 // Tree.
-// WAVE as for the ring: one wave per rank, rank and tree record in scalar
-// registers.
-template <typename R, int ESZ, bool WAVE>
+// RPW: virtual ranks per wave (64 / G).  Every rank of a wave is known to the
+// whole wave (ranks wave*RPW .. wave*RPW + RPW-1), so each rank's record,
+// stage lag and current slice are wave-uniform, and a rank's own input is
+// read with a buffer view based at that slice's cell (scalar registers):
+// one load per rank of the wave, in which only that rank's lanes pass a
+// real offset and every other lane an out-of-range one (the hardware range
+// check returns zeros).  A lane ORs the RPW results of a queue entry when it
+// consumes them.  So no queue entry is ever written by anything but a load,
+// and the wait for an entry counts only the loads issued after it: zeroing
+// an entry in registers for lanes without a slice would make the compiler
+// wait for every load in flight, since the entry may still have a load
+// outstanding.
+template <typename R, int ESZ, int RPW>
 __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTask* __restrict__ tasks,
                                                    const TreeNode* __restrict__ nodes) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_TREE_VPT;
-  constexpr int kPrefetch = WAVE ? EMU_TREE_PREFETCH_WAVE : EMU_TREE_PREFETCH;
+  constexpr uint32_t G = 64u / RPW;
+  constexpr int kPrefetch = RPW == 1 ? EMU_TREE_PREFETCH_WAVE : EMU_TREE_PREFETCH;
   extern __shared__ u32x4 fifo[];   // up[2][N][V][G] then down[2][N][V][G]
-  const uint32_t n = a.nranks, g = WAVE ? 64u : a.group;
-  const uint32_t r = WAVE ? wave_u32<WAVE>(threadIdx.x / 64u) : threadIdx.x / g;
-  const uint32_t p = WAVE ? threadIdx.x % 64u : threadIdx.x % g;
+  const uint32_t n = a.nranks, g = G;
+  const uint32_t wave = wave_u32<true>(threadIdx.x / 64u);
+  const uint32_t grp = RPW == 1 ? 0u : (threadIdx.x % 64u) / G;   // the lane's rank among the wave's
+  const uint32_t r = wave * RPW + grp;
+  const uint32_t p = threadIdx.x % G;
   const bool active = r < n;
   const int H = (int)a.height;
   const uint32_t slice_elems = V * g * unit;
+  // The buffers: each rank of the wave (uniform) for the loads, the lane's
+  // own rank for partial vectors and stores.
+  const char* wsrc[RPW];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const uint32_t rk = wave * RPW + k;
+    wsrc[k] = static_cast<const char*>(a.send[rk < n ? rk : 0]);
+  }
+  const char* const src_r = static_cast<const char*>(a.send[active ? r : 0]);
+  char* const dst_r = static_cast<char*>(a.recv[active ? r : 0]);
   auto up_slot = [&](int parity, uint32_t rank, int v) -> u32x4& {
     return fifo[(((uint32_t)parity * n + rank) * V + v) * g + p];
   };
@@ -342,12 +372,24 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
 
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x) {
     const TreeTask task = tasks[t];
-    const TreeNode rec = nodes[wave_u32<WAVE>(task.channel * n + (active ? r : 0))];
-    struct { int up, down[3]; } me;
-    me.up = (int)wave_u32<WAVE>((uint32_t)(int)rec.up);
+    // the records of the wave's ranks (uniform); the lane's own is one of them
+    int lag_k[RPW];
+    bool live_k[RPW];
+    struct { int up, down[3]; } me = {-1, {-1, -1, -1}};
+    int depth = 0;
 #pragma unroll
-    for (int s = 0; s < 3; ++s) me.down[s] = (int)wave_u32<WAVE>((uint32_t)(int)rec.down[s]);
-    const int depth = (int)wave_u32<WAVE>((uint32_t)(int)rec.depth);
+    for (int k = 0; k < RPW; ++k) {
+      const uint32_t rk = wave * RPW + k;
+      const TreeNode rec = nodes[task.channel * n + (rk < n ? rk : 0)];
+      lag_k[k] = H - rec.depth;
+      live_k[k] = rk < n;
+      if (RPW == 1 || grp == (uint32_t)k) {
+        me.up = rec.up;
+#pragma unroll
+        for (int s = 0; s < 3; ++s) me.down[s] = rec.down[s];
+        depth = rec.depth;
+      }
+    }
     const bool is_root = me.up < 0;
     const bool has_children = me.down[0] >= 0;
     // Slices are the slice-size cells of the global element grid that the
@@ -370,48 +412,43 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
     // same shortcut for the loads was slower on small messages: the loads'
     // offsets are a select already, and the branch only lengthens a stage.)
     auto interior = [&](int q) { return q > 0 && q + 1 < nslices; };
-    // Under WAVE a slice is read with a buffer view based at its cell (whole
-    // vectors without a branch, other lanes read zeros) and a partial vector
-    // at the task end is read when it is consumed (fix_slice), as in the ring.
-    auto load_slice = [&](int q, u32x4 (&x)[V], bool enable) {
-      if constexpr (WAVE) {
-        // The cell's first byte, computed from uniform values only, so that
-        // the view sits in scalar registers (a base computed per lane would
-        // make the compiler loop over the distinct bases of the wave).
-        const auto rs = buffer_view(static_cast<const char*>(a.send[r]) + (first_cell + (uint64_t)q) * slice_elems * ESZ);
+    // Own input of the wave's ranks for stage st + kPrefetch (rank k reduces
+    // slice st - lag_k there): one buffer load per rank, based at its
+    // slice's cell (uniform; computed from uniform values only, so that the
+    // view sits in scalar registers); whole vectors only, a partial vector
+    // at the task end is read when it is consumed (fix_slice).
+    auto load_stage = [&](int st, u32x4 (&x)[RPW][V]) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+        const int qk = st - lag_k[k];
+        const bool en = live_k[k] && qk >= 0 && qk < nslices;
+        const auto rs = buffer_view(wsrc[k] + (first_cell + (uint64_t)(en ? qk : 0)) * slice_elems * ESZ);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           const uint32_t lane = (uint32_t)((v * g + p) * kVecBytes);
-          x[v] = ld_buf(rs, enable && nbytes_of(q, v) == kVecBytes ? lane : kNoLoad);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const int nb = enable ? nbytes_of(q, v) : 0;
-          x[v] = nb ? ld_any(a.send[r], boff_of(q, v), nb) : u32x4{0, 0, 0, 0};
+          const bool mine = RPW == 1 || grp == (uint32_t)k;
+          x[k][v] = ld_buf(rs, en && mine && nbytes_of(qk, v) == kVecBytes ? lane : kNoLoad);
         }
       }
     };
     auto fix_slice = [&](int q, u32x4 (&x)[V]) {
-      if constexpr (WAVE) {
-        if (q + 1 < nslices) return;   // a partial vector can only sit at the task end
+      if (q + 1 < nslices) return;   // a partial vector can only sit at the task end
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const int nb = nbytes_of(q, v);
-          if (nb > 0 && nb < kVecBytes) x[v] = ld_part(a.send[r], boff_of(q, v), nb);
-        }
+      for (int v = 0; v < V; ++v) {
+        const int nb = nbytes_of(q, v);
+        if (nb > 0 && nb < kVecBytes) x[v] = ld_part(src_r, boff_of(q, v), nb);
       }
     };
     auto store_slice = [&](int q, const u32x4 (&x)[V]) {
       if (interior(q)) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) st_vec(a.recv[r], boff_of(q, v), R::post(x[v]));
+        for (int v = 0; v < V; ++v) st_vec(dst_r, boff_of(q, v), R::post(x[v]));
         return;
       }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int nb = nbytes_of(q, v);
-        if (nb) st_any(a.recv[r], boff_of(q, v), nb, R::post(x[v]));
+        if (nb) st_any(dst_r, boff_of(q, v), nb, R::post(x[v]));
       }
     };
     const int up_lag = H - depth;        // reduce slice q at stage q + up_lag
@@ -420,15 +457,15 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
 
     // The own input that a rank reduces at stage st is loaded PF stages
     // earlier into queue entry st mod PF: the stage loop is unrolled by PF,
-    // and at unrolled position i every lane loads the slice it will reduce
+    // and at unrolled position i every rank loads the slice it will reduce
     // PF stages later into entry i and reduces the one in entry i.  The
-    // entry depends on the stage only, not on the rank's lag, so a wave that
-    // holds ranks of different depths (G < 64) uses the same queue.  Every
-    // entry is refilled unconditionally (a load of nothing when there is no
-    // slice), so entries rotate by name and are never merged or copied while
-    // their loads are in flight.  Stages -PF .. -1 only refill; every wave
-    // meets the barriers of stages 0 .. nstages-1 in order.
-    u32x4 q[kPrefetch][V];
+    // entry depends on the stage only, not on the rank's lag, so the ranks of
+    // one wave share the queue.  Every entry is refilled unconditionally (a
+    // load of nothing when there is no slice), so entries rotate by name and
+    // are never merged or copied while their loads are in flight.  Stages
+    // -PF .. -1 only refill; every wave meets the barriers of stages
+    // 0 .. nstages-1 in order.
+    u32x4 q[kPrefetch][RPW][V];
     for (int st0 = -kPrefetch; st0 < nstages; st0 += kPrefetch) {
 #pragma unroll
       for (int i = 0; i < kPrefetch; ++i) {
@@ -439,7 +476,11 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
         if (live && active && qu >= 0 && qu < nslices) {
           u32x4 acc[V];
 #pragma unroll
-          for (int v = 0; v < V; ++v) acc[v] = q[i][v];
+          for (int v = 0; v < V; ++v) {
+            acc[v] = q[i][0][v];
+#pragma unroll
+            for (int k = 1; k < RPW; ++k) acc[v] |= q[i][k][v];
+          }
           fix_slice(qu, acc);
 #pragma unroll
           for (int v = 0; v < V; ++v) acc[v] = R::pre(acc[v]);
@@ -462,10 +503,7 @@ __global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTa
             for (int v = 0; v < V; ++v) up_slot(cur, r, v) = acc[v];
           }
         }
-        {
-          const int qn = qu + kPrefetch;
-          load_slice(qn, q[i], active && qn >= 0 && qn < nslices);
-        }
+        load_stage(st + kPrefetch, q[i]);
         if (live) {
           const int qd = st - dn_lag;
           if (active && !is_root && qd >= 0 && qd < nslices) {
@@ -505,17 +543,21 @@ static hipError_t launch_ring_t(const StepArgs& a, int grid, int block, size_t l
   return a.group == 64 ? launch_ring_w<T, O, COLL, true>(a, grid, block, lds, s)
                        : launch_ring_w<T, O, COLL, false>(a, grid, block, lds, s);
 }
-template <DType T, Op O, bool WAVE>
+template <DType T, Op O, int RPW>
 static hipError_t launch_tree_w(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  if (hipError_t e = allow_lds(step_tree<Red<T, O>, Unit<T>::esz, WAVE>, lds)) return e;
-  hipLaunchKernelGGL((step_tree<Red<T, O>, Unit<T>::esz, WAVE>), dim3(grid), dim3(block), lds, s, a,
+  if (hipError_t e = allow_lds(step_tree<Red<T, O>, Unit<T>::esz, RPW>, lds)) return e;
+  hipLaunchKernelGGL((step_tree<Red<T, O>, Unit<T>::esz, RPW>), dim3(grid), dim3(block), lds, s, a,
                      static_cast<const TreeTask*>(a.tasks), static_cast<const TreeNode*>(a.table));
   return hipGetLastError();
 }
 template <DType T, Op O>
 static hipError_t launch_tree_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  return a.group == 64 ? launch_tree_w<T, O, true>(a, grid, block, lds, s)
-                       : launch_tree_w<T, O, false>(a, grid, block, lds, s);
+  switch (a.group) {
+    case 64: return launch_tree_w<T, O, 1>(a, grid, block, lds, s);
+    case 32: return launch_tree_w<T, O, 2>(a, grid, block, lds, s);
+    case 16: return launch_tree_w<T, O, 4>(a, grid, block, lds, s);
+    default: return hipErrorInvalidValue;   // the planner keeps the group at 16, 32 or 64 lanes
+  }
 }
 
 template <DType T>
@@ -562,10 +604,11 @@ static int occupancy_of(K kernel, int block, size_t lds) {
 }
 
 template <DType T, Op O>
-static int occupancy_t(bool ring, bool wave, int block, size_t lds) {
+static int occupancy_t(bool ring, bool wave, int block, size_t lds, int group) {
   if (!ring)
-    return wave ? occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, true>, block, lds)
-                : occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, false>, block, lds);
+    return group == 64   ? occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, 1>, block, lds)
+           : group == 32 ? occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, 2>, block, lds)
+                         : occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, 4>, block, lds);
   return wave ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, true>, block, lds)
               : occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, false>, block, lds);
 }
@@ -576,16 +619,16 @@ static int occupancy_t(bool ring, bool wave, int block, size_t lds) {
 int stepwise_occupancy(bool ring, DType t, Op op, int block, size_t lds, int group) {
   const bool wave = group == 64;
   switch (t) {
-    case DType::I32: return op == Op::Sum ? occupancy_t<DType::I32, Op::Sum>(ring, wave, block, lds)
-                                          : occupancy_t<DType::I32, Op::Max>(ring, wave, block, lds);
-    case DType::I64: return op == Op::Sum ? occupancy_t<DType::I64, Op::Sum>(ring, wave, block, lds)
-                                          : occupancy_t<DType::I64, Op::Max>(ring, wave, block, lds);
-    case DType::F32: return op == Op::Sum ? occupancy_t<DType::F32, Op::Sum>(ring, wave, block, lds)
-                                          : occupancy_t<DType::F32, Op::Max>(ring, wave, block, lds);
-    case DType::F16: return op == Op::Sum ? occupancy_t<DType::F16, Op::Sum>(ring, wave, block, lds)
-                                          : occupancy_t<DType::F16, Op::Max>(ring, wave, block, lds);
-    case DType::BF16: return op == Op::Sum ? occupancy_t<DType::BF16, Op::Sum>(ring, wave, block, lds)
-                                           : occupancy_t<DType::BF16, Op::Max>(ring, wave, block, lds);
+    case DType::I32: return op == Op::Sum ? occupancy_t<DType::I32, Op::Sum>(ring, wave, block, lds, group)
+                                          : occupancy_t<DType::I32, Op::Max>(ring, wave, block, lds, group);
+    case DType::I64: return op == Op::Sum ? occupancy_t<DType::I64, Op::Sum>(ring, wave, block, lds, group)
+                                          : occupancy_t<DType::I64, Op::Max>(ring, wave, block, lds, group);
+    case DType::F32: return op == Op::Sum ? occupancy_t<DType::F32, Op::Sum>(ring, wave, block, lds, group)
+                                          : occupancy_t<DType::F32, Op::Max>(ring, wave, block, lds, group);
+    case DType::F16: return op == Op::Sum ? occupancy_t<DType::F16, Op::Sum>(ring, wave, block, lds, group)
+                                          : occupancy_t<DType::F16, Op::Max>(ring, wave, block, lds, group);
+    case DType::BF16: return op == Op::Sum ? occupancy_t<DType::BF16, Op::Sum>(ring, wave, block, lds, group)
+                                           : occupancy_t<DType::BF16, Op::Max>(ring, wave, block, lds, group);
   }
   return 1;
 }

@@ -29,6 +29,32 @@
 
 namespace emu {
 
+// Occupancy targets (waves per SIMD the compiler must leave registers for;
+// 0: none), build-time tuning knobs.  A 1024-thread workgroup is 4 waves per
+// SIMD, so two resident workgroups need 8.  Measured on MI355X: the ring
+// with two or four ranks per wave needs 70-91 VGPRs, one workgroup per CU;
+// held to 8 waves (64 VGPRs, a few bytes spilled) it ran 5% faster on 4 x 8
+// ranks i64 and f32 max, 2% slower on f16, within 1% elsewhere.  The tree
+// with two ranks per wave ran 1-3% slower held to 8 waves: its pipeline is
+// then split into twice as many shorter pieces, each paying its fill and
+// drain.
+#ifndef EMU_RING_WAVES_PER_EU
+#define EMU_RING_WAVES_PER_EU 8
+#endif
+#ifndef EMU_TREE_WAVES_PER_EU
+#define EMU_TREE_WAVES_PER_EU 0
+#endif
+#if EMU_RING_WAVES_PER_EU
+#define EMU_RING_OCCUPANCY __attribute__((amdgpu_waves_per_eu(EMU_RING_WAVES_PER_EU)))
+#else
+#define EMU_RING_OCCUPANCY
+#endif
+#if EMU_TREE_WAVES_PER_EU
+#define EMU_TREE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(EMU_TREE_WAVES_PER_EU)))
+#else
+#define EMU_TREE_OCCUPANCY
+#endif
+
 // LDS barrier for step hand-off: LDS writes are complete before the barrier;
 // outstanding global loads (prefetches of the next step) stay in flight.
 __device__ __forceinline__ void step_barrier() {
@@ -102,19 +128,23 @@ __device__ __forceinline__ uint64_t wave_u64(uint64_t x) {
   return x;
 }
 
-template <typename R, int ESZ, int COLL, bool WAVE>
-__global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTask* __restrict__ tasks,
+template <typename R, int ESZ, int COLL, int RPW>
+__global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepArgs a, const RingTask* __restrict__ tasks,
                                                    const RingLoopBlock* __restrict__ loops,
                                                    const uint32_t* __restrict__ orders) {
+  constexpr bool WAVE = RPW == 1;
+  constexpr uint32_t G = 64u / RPW;
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_RING_VPT;
   constexpr int kPrefetch = WAVE ? EMU_RING_PREFETCH_WAVE : EMU_RING_PREFETCH;
   constexpr uint32_t kSkew = COLL == kAllReduce ? EMU_RING_SKEW : 0;
   extern __shared__ u32x4 fifo[];   // slots [2][N][V][G], descriptors [2][N], ring orders [2][kMaxRanks] bytes
-  const uint32_t n = a.nranks, g = WAVE ? 64u : a.group;
-  // r: ring position
-  const uint32_t r = WAVE ? wave_u32<WAVE>(threadIdx.x / 64u) : threadIdx.x / g;
-  const uint32_t p = WAVE ? threadIdx.x % 64u : threadIdx.x % g;
+  const uint32_t n = a.nranks, g = G;
+  // r: ring position (the lane's); the wave holds positions wave*RPW .. wave*RPW + RPW-1
+  const uint32_t wave = wave_u32<true>(threadIdx.x / 64u);
+  const uint32_t grp = WAVE ? 0u : (threadIdx.x % 64u) / G;
+  const uint32_t r = wave * RPW + grp;
+  const uint32_t p = threadIdx.x % G;
   const bool active = r < n;
   const uint32_t prev = active ? (r + n - 1) % n : 0;
   auto slot = [&](uint32_t parity, uint32_t rank, int v) -> u32x4& {
@@ -146,32 +176,47 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
   uint32_t set = 0;
   for (uint32_t t = blockIdx.x; t < a.ntasks; t += gridDim.x, set ^= 1) {
     const RingLoopBlock* blk = desc + set * n;
-    // the rank at position r
+    // The rank at the lane's position, and its buffers, looked up once per
+    // task: with several ranks per wave the rank differs between lanes, and
+    // indexing the argument's pointer table with it is a vector load whose
+    // wait (vmcnt 0) would also wait for every prefetch in flight.
     const uint32_t me = active ? wave_u32<WAVE>(order[set * kMaxRanks + r]) : 0;
-    // Its buffers, looked up once per task.  With G < 64 the rank differs
-    // between the lanes of a wave, and indexing the argument's pointer table
-    // with it is a vector load whose wait (vmcnt 0) would also wait for
-    // every prefetch in flight; read here, that wait happens once per task
-    // instead of at every step.
     const char* const src_me = static_cast<const char*>(a.send[me]);
     char* const dst_me = static_cast<char*>(a.recv[me]);
     // byte distance between a block's place and the rank's own buffer
     const uint64_t my_shift = COLL == kAllReduce ? 0 : (uint64_t)me * a.block * ESZ;
     const uint64_t load_shift = COLL == kAllGather ? my_shift : 0;
     const uint64_t store_shift = COLL == kReduceScatter ? my_shift : 0;
+    // The same for every position of the wave, wave-uniform: the loads of
+    // position k read with a buffer view of that rank's buffer.
+    const char* wsrc[RPW];
+    uint64_t wshift[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const uint32_t rk = wave * RPW + k;
+      const uint32_t mk = wave_u32<true>(order[set * kMaxRanks + (rk < n ? rk : 0)]);
+      wsrc[k] = static_cast<const char*>(a.send[mk]);
+      wshift[k] = COLL == kAllGather ? (uint64_t)mk * a.block * ESZ : 0;
+    }
     if (n > 1) stage_desc(t + gridDim.x, set ^ 1);   // visible after this task's barriers
     // Slice q of block b is the q-th slice-size cell of the global element
     // grid that the block overlaps; lane p's vector v sits at a fixed place in
     // the cell (aligned accesses), and is live only inside the block.
     const uint64_t slice_elems = (uint64_t)V * g * unit;
     // Block b as seen by this task: the first element of its slice cell and
-    // its [start, end) range (wave-uniform under WAVE).
+    // its [start, end) range.  view_u: for a wave-uniform b, in scalar
+    // registers; view_of: for the lane's own block.
     struct View { uint64_t cell, start, end; };
-    auto view_of = [&](uint32_t b) -> View {
+    auto view_u = [&](uint32_t b) -> View {
       const RingLoopBlock d = blk[b];
-      const uint64_t start = wave_u64<WAVE>(d.offset);
-      const uint32_t nelem = wave_u32<WAVE>(d.nelem), cell = wave_u32<WAVE>(d.first_cell);
+      const uint64_t start = wave_u64<true>(d.offset);
+      const uint32_t nelem = wave_u32<true>(d.nelem), cell = wave_u32<true>(d.first_cell);
       return {(uint64_t)cell * slice_elems, start, start + nelem};
+    };
+    auto view_of = [&](uint32_t b) -> View {
+      if constexpr (WAVE) return view_u(b);
+      const RingLoopBlock d = blk[b];
+      return {(uint64_t)d.first_cell * slice_elems, d.offset, d.offset + d.nelem};
     };
     // A cell that lies wholly inside its block: every lane holds a whole
     // vector, so no lane needs its bounds checked.
@@ -181,69 +226,80 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
       const uint64_t left = w.end - pos;
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
-    // Under WAVE a block is read with one buffer view based at its slice
-    // cell: whole vectors load without a branch (other lanes read zeros, the
-    // hardware range check), and a partial vector at the message end is read
-    // when it is consumed (fix_block).
-    auto load_block = [&](uint32_t b, u32x4 (&x)[V], bool enable) {
-      const View w = view_of(b);
-      const char* const src = src_me;
-      if constexpr (WAVE) {
-        const auto rs = buffer_view(src + (w.cell * ESZ - load_shift));
-        if (enable && whole(w)) {
+    // Loads block bk[k] of the rank at position k of the wave into x[k], for
+    // every k: one buffer view per position based at the block's slice cell
+    // (uniform), in which only that position's lanes pass a real offset
+    // (whole vectors; other lanes read zeros, the hardware range check).  A
+    // partial vector at the message end is read when it is consumed
+    // (fix_block).  Issued for the whole wave, outside any per-lane branch,
+    // and never into a register that anything but a load writes.
+    auto load_blocks = [&](const uint32_t (&bk)[RPW], u32x4 (&x)[RPW][V], bool enable) {
 #pragma unroll
-          for (int v = 0; v < V; ++v) x[v] = ld_buf(rs, (uint32_t)((v * g + p) * kVecBytes));
+      for (int k = 0; k < RPW; ++k) {
+        const bool en = enable && wave * RPW + k < n;
+        const View w = view_u(bk[k]);
+        const auto rs = buffer_view(wsrc[k] + (w.cell * ESZ - wshift[k]));
+        const bool mine = WAVE || grp == (uint32_t)k;
+        if (en && whole(w)) {
+#pragma unroll
+          for (int v = 0; v < V; ++v) x[k][v] = ld_buf(rs, mine ? (uint32_t)((v * g + p) * kVecBytes) : kNoLoad);
         } else {
 #pragma unroll
           for (int v = 0; v < V; ++v) {
             const uint32_t lane = (uint32_t)((v * g + p) * unit);
-            x[v] = ld_buf(rs, enable && nbytes_of(w, w.cell + lane) == kVecBytes ? lane * ESZ : kNoLoad);
+            x[k][v] = ld_buf(rs, en && mine && nbytes_of(w, w.cell + lane) == kVecBytes ? lane * ESZ : kNoLoad);
           }
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
-          const int nb = enable ? nbytes_of(w, pos) : 0;
-          x[v] = nb ? ld_any(src, pos * ESZ - load_shift, nb) : u32x4{0, 0, 0, 0};
         }
       }
     };
-    auto fix_block = [&](uint32_t b, u32x4 (&x)[V]) {
-      if constexpr (WAVE) {
-        const View w = view_of(b);
-        if (w.cell + slice_elems <= w.end) return;   // a partial vector can only sit at the block end
+    auto take = [&](const u32x4 (&x)[RPW][V], u32x4 (&out)[V]) {
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-          const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
-          const int nb = nbytes_of(w, pos);
-          if (nb > 0 && nb < kVecBytes) x[v] = ld_part(src_me, pos * ESZ - load_shift, nb);
-        }
+      for (int v = 0; v < V; ++v) {
+        out[v] = x[0][v];
+#pragma unroll
+        for (int k = 1; k < RPW; ++k) out[v] |= x[k][v];
+      }
+    };
+    auto fix_block = [&](uint32_t b, u32x4 (&x)[V]) {
+      const View w = view_of(b);
+      if (w.cell + slice_elems <= w.end) return;   // a partial vector can only sit at the block end
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
+        const int nb = nbytes_of(w, pos);
+        if (nb > 0 && nb < kVecBytes) x[v] = ld_part(src_me, pos * ESZ - load_shift, nb);
       }
     };
     auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
       const View w = view_of(b);
-      char* const dst = dst_me;
       if (whole(w)) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
-          st_vec(dst, (w.cell + (uint32_t)((v * g + p) * unit)) * ESZ - store_shift, R::post(x[v]));
+          st_vec(dst_me, (w.cell + (uint32_t)((v * g + p) * unit)) * ESZ - store_shift, R::post(x[v]));
         return;
       }
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const uint64_t pos = w.cell + (uint32_t)((v * g + p) * unit);
         const int nb = nbytes_of(w, pos);
-        if (nb) st_any(dst, pos * ESZ - store_shift, nb, R::post(x[v]));
+        if (nb) st_any(dst_me, pos * ESZ - store_shift, nb, R::post(x[v]));
       }
     };
+    // the positions of the wave, for block indices counted per position
+    uint32_t pos_k[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+      const uint32_t rk = wave * RPW + k;
+      pos_k[k] = rk < n ? rk : 0;
+    }
 
     if (n == 1) {
+      u32x4 x[RPW][V], own[V];
+      load_blocks(pos_k, x, true);
       if (active) {
-        u32x4 x[V];
-        load_block(0, x, true);
-        fix_block(0, x);
-        store_block(0, x);
+        take(x, own);
+        fix_block(0, own);
+        store_block(0, own);
       }
       // one rank: no steps, so stage the next descriptor here
       step_barrier();
@@ -254,9 +310,14 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
     if constexpr (COLL == kAllGather) {
       // the position's own input is the finished block (r+1) mod N: write it
       // to its own output and into the slot the forwarding steps read first
+      uint32_t bk[RPW];
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) bk[k] = pos_k[k] + 1 == n ? 0 : pos_k[k] + 1;
+      u32x4 x[RPW][V];
+      load_blocks(bk, x, true);
       if (active) {
         u32x4 own[V];
-        load_block((r + 1) % n, own, true);
+        take(x, own);
         fix_block((r + 1) % n, own);
         store_block((r + 1) % n, own);
 #pragma unroll
@@ -265,32 +326,45 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
       step_barrier();
     } else {
     // step 0: send own block r; the blocks of steps 1..PF are loaded ahead
-    // (queue q[0] is the next step's block).
-    u32x4 own[V], q[kPrefetch][V];
+    // (queue q[0] is the next step's block).  Block of step s at position
+    // k: (k - s) mod N, counted down per position.
+    u32x4 own[RPW][V], q[kPrefetch][RPW][V];
+    uint32_t bpf[RPW];
+    load_blocks(pos_k, own, true);
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) bpf[k] = pos_k[k];
+#pragma unroll
+    for (int i = 0; i < kPrefetch; ++i) {
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) bpf[k] = bpf[k] == 0 ? n - 1 : bpf[k] - 1;
+      load_blocks(bpf, q[i], (uint32_t)i + 1 < n);
+    }
     if (active) {
-      load_block(r, own, true);
+      u32x4 mine[V];
+      take(own, mine);
+      fix_block(r, mine);
 #pragma unroll
-      for (int i = 0; i < kPrefetch; ++i)
-        if ((uint32_t)i + 1 < n) load_block((r + 2 * n - 1 - i) % n, q[i], true);
-      fix_block(r, own);
-#pragma unroll
-      for (int v = 0; v < V; ++v) slot(0, r, v) = R::pre(own[v]);
+      for (int v = 0; v < V; ++v) slot(0, r, v) = R::pre(mine[v]);
     }
     step_barrier();
-    // block of step s, (r - s) mod N, and of step s + PF, counted down step by step
-    uint32_t b = r, bpf = (r + 2 * n - kPrefetch) % n;
+    // the lane's block of step s, (r - s) mod N, counted down step by step
+    uint32_t b = r;
     for (uint32_t s = 1; s < n; ++s) {
       b = b == 0 ? n - 1 : b - 1;
-      bpf = bpf == 0 ? n - 1 : bpf - 1;
+      u32x4 mine[V];
+      take(q[0], mine);   // this step's entry (waits for its loads only)
+#pragma unroll
+      for (int i = 0; i + 1 < kPrefetch; ++i)
+#pragma unroll
+        for (int k = 0; k < RPW; ++k)
+#pragma unroll
+          for (int v = 0; v < V; ++v) q[i][k][v] = q[i + 1][k][v];
+      if (s + kPrefetch < n) {
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) bpf[k] = bpf[k] == 0 ? n - 1 : bpf[k] - 1;
+        load_blocks(bpf, q[kPrefetch - 1], true);
+      }
       if (active) {
-        u32x4 mine[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) mine[v] = q[0][v];
-#pragma unroll
-        for (int i = 0; i + 1 < kPrefetch; ++i)
-#pragma unroll
-          for (int v = 0; v < V; ++v) q[i][v] = q[i + 1][v];
-        if (s + kPrefetch < n) load_block(bpf, q[kPrefetch - 1], true);
         fix_block(b, mine);
         u32x4 res[V];
 #pragma unroll
@@ -338,7 +412,7 @@ __global__ __launch_bounds__(1024) void step_ring(const StepArgs a, const RingTa
 // wait for every load in flight, since the entry may still have a load
 // outstanding.
 template <typename R, int ESZ, int RPW>
-__global__ __launch_bounds__(1024) void step_tree(const StepArgs a, const TreeTask* __restrict__ tasks,
+__global__ __launch_bounds__(1024) EMU_TREE_OCCUPANCY void step_tree(const StepArgs a, const TreeTask* __restrict__ tasks,
                                                    const TreeNode* __restrict__ nodes) {
   constexpr int unit = kVecBytes / ESZ;
   constexpr int V = EMU_TREE_VPT;
@@ -531,17 +605,21 @@ static hipError_t allow_lds(K kernel, size_t lds) {
                              (int)lds);
 }
 
-template <DType T, Op O, int COLL, bool WAVE>
+template <DType T, Op O, int COLL, int RPW>
 static hipError_t launch_ring_w(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz, COLL, WAVE>, lds)) return e;
-  hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz, COLL, WAVE>), dim3(grid), dim3(block), lds, s, a,
+  if (hipError_t e = allow_lds(step_ring<Red<T, O>, Unit<T>::esz, COLL, RPW>, lds)) return e;
+  hipLaunchKernelGGL((step_ring<Red<T, O>, Unit<T>::esz, COLL, RPW>), dim3(grid), dim3(block), lds, s, a,
                      static_cast<const RingTask*>(a.tasks), static_cast<const RingLoopBlock*>(a.table), a.orders);
   return hipGetLastError();
 }
 template <DType T, Op O, int COLL>
 static hipError_t launch_ring_t(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
-  return a.group == 64 ? launch_ring_w<T, O, COLL, true>(a, grid, block, lds, s)
-                       : launch_ring_w<T, O, COLL, false>(a, grid, block, lds, s);
+  switch (a.group) {
+    case 64: return launch_ring_w<T, O, COLL, 1>(a, grid, block, lds, s);
+    case 32: return launch_ring_w<T, O, COLL, 2>(a, grid, block, lds, s);
+    case 16: return launch_ring_w<T, O, COLL, 4>(a, grid, block, lds, s);
+    default: return hipErrorInvalidValue;   // the planner keeps the group at 16, 32 or 64 lanes
+  }
 }
 template <DType T, Op O, int RPW>
 static hipError_t launch_tree_w(const StepArgs& a, int grid, int block, size_t lds, hipStream_t s) {
@@ -609,8 +687,9 @@ static int occupancy_t(bool ring, bool wave, int block, size_t lds, int group) {
     return group == 64   ? occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, 1>, block, lds)
            : group == 32 ? occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, 2>, block, lds)
                          : occupancy_of(step_tree<Red<T, O>, Unit<T>::esz, 4>, block, lds);
-  return wave ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, true>, block, lds)
-              : occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, false>, block, lds);
+  return group == 64   ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, 1>, block, lds)
+         : group == 32 ? occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, 2>, block, lds)
+                       : occupancy_of(step_ring<Red<T, O>, Unit<T>::esz, kAllReduce, 4>, block, lds);
 }
 
 // Resident workgroups per CU for the stepwise kernels at this block/LDS size

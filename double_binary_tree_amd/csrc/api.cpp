@@ -397,17 +397,29 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
 // (us per dependent stage, the fixed cost of a call folded in) and the
 // bandwidth B (bytes/us).  Predicted time of S bytes per rank:
 //   ring 2(N-1)*alpha + 2(N-1)/N * S/B,   tree 2*D*alpha + 2*S/B,
-// D the deepest channel tree.  Defaults: least-squares fit to the 12-channel
-// message-size sweep of 8 ranks on one node measured on MI355X.
+// D the deepest channel tree.  The parameters are kept per rank-count
+// class, since the emulation's cost per stage and per byte changes with N
+// (one, two or four virtual ranks per wave; deeper trees): classes are
+// centred on the measured 8, 16 and 32 ranks, with boundaries at their
+// geometric midpoints.
+constexpr int kCostClasses = 3;
+int cost_class(int nranks) { return nranks * nranks <= 128 ? 0 : nranks * nranks <= 512 ? 1 : 2; }
 struct Cost { double alpha_us, bw; };
-Cost g_cost[2][2] = {          // [stepwise, fused][ring, tree]
-    {{1.10419, 625415.0}, {1.09448, 659195.0}},
-    {{0.672418, 631521.0}, {0.632165, 737631.0}},
+// Defaults: least-squares fits to message-size sweeps measured on MI355X
+// (graph-replayed launches, library buffer placement): 8 ranks on one node,
+// f32, 12 channels; 16 ranks on 16 nodes, bf16, 8 channels; 4 x 8 ranks,
+// f16, 16 channels.  The points are kept in the repository's profiles
+// (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
+// prints this table.
+Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
+    {{{0.628749, 670837}, {0.548981, 682840}}, {{0.194137, 640335}, {0.165065, 802097}}},   // 8 ranks
+    {{{0.655195, 486332}, {1.01295, 341953}}, {{0.131108, 413158}, {0.659806, 455341}}},    // 16 ranks
+    {{{0.690267, 230339}, {0.87316, 176326}}, {{0.0808736, 199172}, {0.423295, 220534}}},   // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {
-  const Cost& k = g_cost[fused ? 1 : 0][algo == Algo::Ring ? 0 : 1];
   const int n = c.nranks;
+  const Cost& k = g_cost[cost_class(n)][fused ? 1 : 0][algo == Algo::Ring ? 0 : 1];
   if (algo == Algo::Ring) return (double)(2 * (n - 1)) * k.alpha_us + 2.0 * (n - 1) / n * nbytes / k.bw;
   int depth = 0;
   for (const auto& ch : c.topo.channels) depth = std::max(depth, ch.height);
@@ -701,13 +713,31 @@ int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t 
   return run_collective(kAllGather, sendbufs, recvbufs, sendcount, dtype, EMU_SUM, stream);
 }
 
-int emu_set_cost_model(int algo, double alpha_us, double bw_bytes_per_us) {
+int emu_set_cost_model_ranks(int algo, int nranks, double alpha_us, double bw_bytes_per_us) {
   const int base = algo & 0xFF, mode = algo & ~0xFF;
   if ((base != EMU_ALGO_RING && base != EMU_ALGO_TREE) || (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED))
     return EMU_ERR_INVALID_ARGUMENT;
+  if (nranks != 0 && (nranks < 1 || nranks > kMaxRanks)) return EMU_ERR_INVALID_ARGUMENT;
   if (!(alpha_us >= 0.0) || !(bw_bytes_per_us > 0.0) || alpha_us > 1e9 || bw_bytes_per_us > 1e15)
     return EMU_ERR_INVALID_ARGUMENT;
-  g_cost[mode == EMU_MODE_FUSED ? 1 : 0][base == EMU_ALGO_RING ? 0 : 1] = {alpha_us, bw_bytes_per_us};
+  for (int k = 0; k < kCostClasses; ++k)
+    if (nranks == 0 || k == cost_class(nranks))
+      g_cost[k][mode == EMU_MODE_FUSED ? 1 : 0][base == EMU_ALGO_RING ? 0 : 1] = {alpha_us, bw_bytes_per_us};
+  return EMU_SUCCESS;
+}
+
+int emu_set_cost_model(int algo, double alpha_us, double bw_bytes_per_us) {
+  return emu_set_cost_model_ranks(algo, 0, alpha_us, bw_bytes_per_us);
+}
+
+int emu_get_cost_model(int algo, int nranks, double* alpha_us, double* bw_bytes_per_us) {
+  const int base = algo & 0xFF, mode = algo & ~0xFF;
+  if ((base != EMU_ALGO_RING && base != EMU_ALGO_TREE) || (mode != EMU_MODE_STEPWISE && mode != EMU_MODE_FUSED))
+    return EMU_ERR_INVALID_ARGUMENT;
+  if (nranks < 1 || nranks > kMaxRanks || !alpha_us || !bw_bytes_per_us) return EMU_ERR_INVALID_ARGUMENT;
+  const Cost& k = g_cost[cost_class(nranks)][mode == EMU_MODE_FUSED ? 1 : 0][base == EMU_ALGO_RING ? 0 : 1];
+  *alpha_us = k.alpha_us;
+  *bw_bytes_per_us = k.bw;
   return EMU_SUCCESS;
 }
 

@@ -69,6 +69,11 @@ def lib() -> ctypes.CDLL:
         L.emu_comm_destroy.restype = ctypes.c_int
         L.emu_set_cost_model.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
         L.emu_set_cost_model.restype = ctypes.c_int
+        L.emu_set_cost_model_ranks.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.emu_set_cost_model_ranks.restype = ctypes.c_int
+        L.emu_get_cost_model.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_double)]
+        L.emu_get_cost_model.restype = ctypes.c_int
         L.emu_predict_us.argtypes = [ctypes.c_int, ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
         L.emu_predict_us.restype = ctypes.c_int
         L.emu_select_algo.argtypes = [ctypes.c_size_t, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -179,6 +184,21 @@ def all_gather(sendptrs, recvptrs, sendcount: int, dtype: str, stream: int = 0) 
 
 def set_cost_model(algo: str, mode: str, alpha_us: float, bw_bytes_per_us: float) -> None:
     _check(lib().emu_set_cost_model(algo_code(algo, mode), alpha_us, bw_bytes_per_us), "emu_set_cost_model")
+
+
+def set_cost_model_ranks(algo: str, mode: str, nranks: int, alpha_us: float, bw_bytes_per_us: float) -> None:
+    """emu_set_cost_model_ranks: the parameters of the rank-count class of
+    ``nranks`` (0: every class)."""
+    _check(lib().emu_set_cost_model_ranks(algo_code(algo, mode), nranks, alpha_us, bw_bytes_per_us),
+           "emu_set_cost_model_ranks")
+
+
+def get_cost_model(algo: str, mode: str, nranks: int) -> tuple[float, float]:
+    """(alpha us per stage, bandwidth bytes/us) of the class of ``nranks``."""
+    a, b = ctypes.c_double(), ctypes.c_double()
+    _check(lib().emu_get_cost_model(algo_code(algo, mode), nranks, ctypes.byref(a), ctypes.byref(b)),
+           "emu_get_cost_model")
+    return a.value, b.value
 
 
 def predict_us(algo: str, mode: str, count: int, dtype: str) -> float:

@@ -291,16 +291,23 @@ int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t 
  * ranks, D the deepest channel tree):
  *   ring: 2(N-1) * alpha + 2(N-1)/N * S / bw
  *   tree: 2 * D * alpha  + 2 * S / bw
- * (microseconds; the fixed cost of a call is folded into alpha).  The
- * defaults are a least-squares fit to a message-size sweep of 8 ranks on one
- * node measured on MI355X (per mode).  Selection takes the smaller predicted
+ * (microseconds; the fixed cost of a call is folded into alpha).  alpha
+ * and bw are kept per (mode, algorithm) and per rank-count class: N <= 11,
+ * 12 <= N <= 22, N >= 23 (centred on 8, 16 and 32 ranks; on one GPU the
+ * cost per stage and per byte changes with the number of virtual ranks).
+ * The defaults are least-squares fits to message-size sweeps measured on
+ * MI355X at 8, 16 and 32 ranks.  Selection takes the smaller predicted
  * time, the ring on an exact tie (page "NCCL代码分析", section "通讯时如何选择
  * Channel": the algorithm of least predicted time is used).
  *
  * emu_set_cost_model - replace alpha (us per stage, >= 0) and bw (bytes per
  *   us, > 0) of `algo` (EMU_ALGO_RING or EMU_ALGO_TREE, optionally |
- *   EMU_MODE_FUSED); process-wide, host only.  EMU_ERR_INVALID_ARGUMENT for
- *   other algorithms or values out of range (state unchanged).
+ *   EMU_MODE_FUSED) in every rank-count class; process-wide, host only.
+ *   EMU_ERR_INVALID_ARGUMENT for other algorithms or values out of range
+ *   (state unchanged).
+ * emu_set_cost_model_ranks - the same for the class of `nranks` only (1 ..
+ *   EMU_MAX_RANKS; 0 means every class).
+ * emu_get_cost_model - alpha and bw of `algo` in the class of `nranks`.
  * emu_predict_us - the predicted time of one all-reduce of `count` elements of
  *   `dtype` with `algo` (as above) on the active communicator, into *us.
  * emu_select_algo - the algorithm an all-reduce of `count` elements of
@@ -311,6 +318,8 @@ int emu_all_gather(const void* const sendbufs[], void* const recvbufs[], size_t 
  * output, unknown dtype or algorithm.
  */
 int emu_set_cost_model(int algo, double alpha_us, double bw_bytes_per_us);
+int emu_set_cost_model_ranks(int algo, int nranks, double alpha_us, double bw_bytes_per_us);
+int emu_get_cost_model(int algo, int nranks, double* alpha_us, double* bw_bytes_per_us);
 int emu_predict_us(int algo, size_t count, int dtype, double* us);
 int emu_select_algo(size_t count, int dtype, int* algo);
 

@@ -13,8 +13,14 @@ from tests.gpu_util import announce, run_allreduce
 
 pytestmark = pytest.mark.gpu
 
-DEFAULTS = {("stepwise", "ring"): (1.10419, 625415.0), ("stepwise", "tree"): (1.09448, 659195.0),
-            ("fused", "ring"): (0.672418, 631521.0), ("fused", "tree"): (0.632165, 737631.0)}
+CLASS_RANKS = (8, 16, 32)       # one rank count inside each rank-count class of the cost model
+DEFAULTS = {}
+
+
+def _restore():
+    from double_binary_tree_amd import emucomm as E
+    for (mode, algo, n), (a, b) in DEFAULTS.items():
+        E.set_cost_model_ranks(algo, mode, n, a, b)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -24,9 +30,12 @@ def _gpu():
         pytest.skip("no GPU")
     from double_binary_tree_amd import emucomm as E
     E.lib()
+    for mode in ("stepwise", "fused"):
+        for algo in ("ring", "tree"):
+            for n in CLASS_RANKS:
+                DEFAULTS[(mode, algo, n)] = E.get_cost_model(algo, mode, n)
     yield
-    for (mode, algo), (a, b) in DEFAULTS.items():
-        E.set_cost_model(algo, mode, a, b)
+    _restore()
     E.comm_destroy()
 
 
@@ -57,5 +66,4 @@ def test_auto_runs_the_selected_algorithm(name, mode):
                 assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(want).view(np.uint8))
         assert seen == {"ring", "tree"}
     finally:
-        for (m, algo), (a, b) in DEFAULTS.items():
-            E.set_cost_model(algo, m, a, b)
+        _restore()

@@ -262,13 +262,22 @@ def test_collective_argument_errors_without_gpu():
     assert ag(send, recv, 1 << 60, 2) == E.ERR_INVALID_ARGUMENT
 
 
-DEFAULT_COST = {("stepwise", "ring"): (1.10419, 625415.0), ("stepwise", "tree"): (1.09448, 659195.0),
-                ("fused", "ring"): (0.672418, 631521.0), ("fused", "tree"): (0.632165, 737631.0)}
+CLASS_RANKS = (8, 16, 32)       # one rank count inside each rank-count class of the cost model
+_defaults = {}
+
+
+def _snapshot_cost():
+    if not _defaults:
+        for mode in ("stepwise", "fused"):
+            for algo in ("ring", "tree"):
+                for n in CLASS_RANKS:
+                    _defaults[(mode, algo, n)] = E.get_cost_model(algo, mode, n)
+    return _defaults
 
 
 def _restore_cost():
-    for (mode, algo), (a, b) in DEFAULT_COST.items():
-        E.set_cost_model(algo, mode, a, b)
+    for (mode, algo, n), (a, b) in _snapshot_cost().items():
+        E.set_cost_model_ranks(algo, mode, n, a, b)
 
 
 @pytest.mark.parametrize("n,m,nch", [(8, 1, 12), (16, 16, 8), (15, 15, 8), (32, 4, 16), (4, 2, 2), (64, 8, 8)])
@@ -285,14 +294,41 @@ def test_cost_model_predictions_and_selection_match_the_oracle(n, m, nch, mode):
             if params is not None:
                 E.set_cost_model("ring", mode, *params[0])
                 E.set_cost_model("tree", mode, *params[1])
-            ring = DEFAULT_COST[(mode, "ring")] if params is None else params[0]
-            tree = DEFAULT_COST[(mode, "tree")] if params is None else params[1]
+            ring = E.get_cost_model("ring", mode, n) if params is None else params[0]
+            tree = E.get_cost_model("tree", mode, n) if params is None else params[1]
             for dtype, esz in (("f32", 4), ("bf16", 2), ("i64", 8)):
                 for count in [0, 1, 7, 1000, 1 << 12, 1 << 16, 123457, 1 << 20, 1 << 24, 3 << 26]:
                     s = float(count) * esz
                     assert E.predict_us("ring", mode, count, dtype) == CM.ring_time(n, s, *ring)
                     assert E.predict_us("tree", mode, count, dtype) == CM.tree_time(depth, s, *tree)
                     assert E.select_algo(count, dtype) == CM.select(n, depth, s, ring + (0.0,), tree + (0.0,))
+    finally:
+        _restore_cost()
+
+
+def test_cost_model_classes_by_rank_count():
+    # The parameters of one rank-count class apply to every communicator of
+    # that class and to no other: N <= 11, 12 <= N <= 22, N >= 23.
+    _restore_cost()
+    try:
+        E.set_cost_model_ranks("ring", "stepwise", 16, 3.25, 12345.0)
+        for n in (1, 8, 11, 12, 16, 22, 23, 32, 64):
+            got = E.get_cost_model("ring", "stepwise", n)
+            assert (got == (3.25, 12345.0)) == (12 <= n <= 22), n
+            E.comm_init(n, 1, "auto", 2, 1 << 19)
+            want = 2 * (n - 1) * got[0] + 2.0 * (n - 1) / n * 4000.0 / got[1]
+            assert E.predict_us("ring", "stepwise", 1000, "f32") == want
+        E.set_cost_model("tree", "fused", 1.5, 5000.0)       # every class
+        for n in CLASS_RANKS:
+            assert E.get_cost_model("tree", "fused", n) == (1.5, 5000.0)
+        L = E.lib()
+        import ctypes
+        a, b = ctypes.c_double(), ctypes.c_double()
+        assert L.emu_set_cost_model_ranks(0, 65, 1.0, 1.0) == E.ERR_INVALID_ARGUMENT
+        assert L.emu_set_cost_model_ranks(0, -1, 1.0, 1.0) == E.ERR_INVALID_ARGUMENT
+        assert L.emu_get_cost_model(0, 0, ctypes.byref(a), ctypes.byref(b)) == E.ERR_INVALID_ARGUMENT
+        assert L.emu_get_cost_model(2, 8, ctypes.byref(a), ctypes.byref(b)) == E.ERR_INVALID_ARGUMENT
+        assert L.emu_get_cost_model(0, 8, None, ctypes.byref(b)) == E.ERR_INVALID_ARGUMENT
     finally:
         _restore_cost()
 

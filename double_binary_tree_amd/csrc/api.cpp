@@ -322,7 +322,7 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     // a grid apart) measured slower from 128 MiB per rank on MI355X (8 ranks
     // f32: 256 MiB 818 -> 763 us, 128 MiB 401 -> 379 us, smaller unchanged).
     // The dispatch holds the grid in work-items as a 32-bit count, so beyond
-    // 2^22 tiles (16 GiB per rank) the workgroups walk the rest grid-strided.
+    // 2^22 tiles (8 GiB per rank) the workgroups walk the rest grid-strided.
     // Debug knob EMU_FUSED_BLOCKS_PER_CU caps the grid at that many per CU.
     constexpr uint64_t kMaxFusedGrid = (uint64_t)1 << 22;
     const long per_cu = env_long("EMU_FUSED_BLOCKS_PER_CU", 0);

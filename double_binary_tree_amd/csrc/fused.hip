@@ -21,8 +21,13 @@
 
 namespace emu {
 
+// Lanes per tile (a tile is one vector per lane of every rank: 2 KiB per
+// rank).  Measured on MI355X against 256 and 512 lanes (3 alternating
+// rounds): 8 ranks f32 1.4-2.5% faster than 256 from 16 to 256 MiB per
+// rank, 16 and 32 ranks within 0.3%; 512 lanes won only at 16 MiB per rank
+// and lost 1-2% elsewhere.
 #ifndef EMU_FUSED_THREADS
-#define EMU_FUSED_THREADS 256
+#define EMU_FUSED_THREADS 128
 #endif
 constexpr int kFusedThreads = EMU_FUSED_THREADS;
 #ifndef EMU_FUSED_VPT
@@ -208,8 +213,9 @@ __device__ __forceinline__ void do_positions(const FusedArgs& a, const uint32_t*
   }
 }
 
-// A tile holds kFusedThreads * kVpt vectors; lane l owns vectors l, l + 256,
-// ... (each group of 64 lanes touches 1 KiB contiguous per rank).  Tiles
+// A tile holds kFusedThreads * kVpt vectors; lane l owns vectors l,
+// l + kFusedThreads, ... (each group of 64 lanes touches 1 KiB contiguous
+// per rank).  Tiles
 // are laid on the input positions (all-reduce, reduce-scatter) or the
 // output positions (all-gather): the side with N accesses per position.
 // The tile table and the order rows come as their own read-only arguments
@@ -229,7 +235,7 @@ __global__ __launch_bounds__(kFusedThreads) void fused_collective(const FusedArg
     const uint64_t base = tile.start * ESZ;
     const uint32_t lane_off = threadIdx.x * kVecBytes;
     if (tile.nelem == kFusedThreads * kVpt * unit) {
-      if (MODE == kProgram) {
+      if constexpr (MODE == kProgram) {
         // The register stack is indexed dynamically; one position at a time
         // keeps it in VGPRs.
         for (int v = 0; v < kVpt; ++v)

@@ -12,7 +12,9 @@ process, so that one profiler run covers them.
 
 A leg is WORKLOAD[@MIB]:ALGO:MODE[:CHANNELS]; @MIB sets the per-rank size
 in MiB (default: the workload's own), CHANNELS the channel count (default:
-the workload's own).
+the workload's own).  A leg stream:KIND:MIB runs the library's streaming
+kernel KIND (read, write or copy) over MIB MiB of HBM traffic (a copy reads
+and writes half of it each), the same-run yardstick at that size.
 """
 
 from __future__ import annotations
@@ -65,6 +67,26 @@ def _main() -> int:
         del src, dst
         torch.cuda.empty_cache()
     for spec in args.leg:
+        if spec.startswith("stream:"):
+            _, kind, mib = spec.split(":")
+            nbytes = int(mib) << 20
+            size = nbytes // 2 if kind == "copy" else nbytes
+            src = torch.ones(size // 4, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                E.stream_probe(kind, src.data_ptr(), dst.data_ptr(), size, stream.cuda_stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.iters):
+                E.stream_probe(kind, src.data_ptr(), dst.data_ptr(), size, stream.cuda_stream)
+            b.record(stream)
+            b.synchronize()
+            us = a.elapsed_time(b) * 1e3 / args.iters
+            print(f"{spec}: {us:.1f} us per launch, {nbytes / us / 1e3:.0f} GB/s ({nbytes / us / 1e3 / 80:.1f}% of "
+                  f"8 TB/s)", flush=True)
+            del src, dst
+            torch.cuda.empty_cache()
+            continue
         w, count, algo, mode, nch = parse_leg(spec)
         dt = getattr(torch, TORCH_DTYPES[w.dtype])
         pool, sends, recvs = E.rank_buffers(w.nranks, count, dt)

@@ -237,8 +237,8 @@ int emu_allreduce(const void* const sendbufs[], void* const recvbufs[], size_t c
  * and stepwise (SIMPLE or LL; an LL abandon is reported by
  * emu_protocol_status).  Additional errors: EMU_ERR_INVALID_ARGUMENT for an
  * EMU_TRANSPORT_DEVICE communicator (its FIFOs are far larger than the
- * array) and for a call whose tables exceed the array (from about 1 GiB per
- * rank in fused mode; the stepwise tables are much smaller).
+ * array) and for a call whose tables exceed the array (from about 512 MiB
+ * per rank in fused mode; the stepwise tables are much smaller).
  */
 #define EMU_NOALLOC_SCRATCH_BYTES (4u << 20)
 int emu_allreduce_noalloc(const void* const sendbufs[], void* const recvbufs[], size_t count,

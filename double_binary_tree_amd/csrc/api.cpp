@@ -412,9 +412,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.628749, 670837}, {0.548981, 682840}}, {{0.194137, 640335}, {0.165065, 802097}}},   // 8 ranks
-    {{{0.655195, 486332}, {1.01295, 341953}}, {{0.131108, 413158}, {0.659806, 455341}}},    // 16 ranks
-    {{{0.690267, 230339}, {0.87316, 176326}}, {{0.0808736, 199172}, {0.423295, 220534}}},   // 32 ranks
+    {{{0.627389, 669774}, {0.547849, 682402}}, {{0.192863, 665572}, {0.164171, 813924}}},   // 8 ranks
+    {{{0.653504, 481792}, {1.01233, 341359}}, {{0.129828, 414881}, {0.655643, 447901}}},    // 16 ranks
+    {{{0.689327, 229263}, {0.872081, 175906}}, {{0.0806491, 198835}, {0.414628, 218616}}},  // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

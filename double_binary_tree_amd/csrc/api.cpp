@@ -800,7 +800,7 @@ int emu_device_memory(size_t* allocations, size_t* bytes) {
 }
 
 int emu_buffer_layout(size_t nbufs, size_t bytes, size_t offsets[], size_t* pool_bytes) {
-  constexpr size_t kSlotAlign = (size_t)64 << 10, kStagger = (size_t)4 << 10;
+  constexpr size_t kSlotAlign = (size_t)64 << 10, kStagger = (size_t)6 << 10;
   if (nbufs == 0 || !offsets || !pool_bytes) return EMU_ERR_INVALID_ARGUMENT;
   if (bytes > SIZE_MAX - 2 * kSlotAlign) return EMU_ERR_INVALID_ARGUMENT;
   const size_t slot = (bytes + kSlotAlign - 1) / kSlotAlign * kSlotAlign + kStagger;

@@ -31,13 +31,14 @@ namespace emu {
 
 // Occupancy targets (waves per SIMD the compiler must leave registers for;
 // 0: none), build-time tuning knobs.  A 1024-thread workgroup is 4 waves per
-// SIMD, so two resident workgroups need 8.  Measured on MI355X: the ring
-// with two or four ranks per wave needs 70-91 VGPRs, one workgroup per CU;
-// held to 8 waves (64 VGPRs, a few bytes spilled) it ran 5% faster on 4 x 8
-// ranks i64 and f32 max, 2% slower on f16, within 1% elsewhere.  The tree
-// with two ranks per wave ran 1-3% slower held to 8 waves: its pipeline is
-// then split into twice as many shorter pieces, each paying its fill and
-// drain.
+// SIMD, so two resident workgroups need 8.  Measured on MI355X (3
+// alternating rounds against the uncapped build): the ring with two or four
+// ranks per wave needs 70-91 VGPRs, one workgroup per CU; held to 8 waves
+// (64 VGPRs, 24-120 bytes per lane spilled) it ran 13% faster on 4 x 8 ranks
+// f16, 7% on 16 ranks bf16, 5% on 4 x 8 ranks i64, and within 0.5% with 8
+// ranks and for the standalone reduce-scatter and all-gather.  The tree with
+// two ranks per wave ran 1-3% slower held to 8 waves: its pipeline is then
+// split into twice as many shorter pieces, each paying its fill and drain.
 #ifndef EMU_RING_WAVES_PER_EU
 #define EMU_RING_WAVES_PER_EU 8
 #endif

@@ -377,14 +377,17 @@ int emu_protocol_status(int* abandoned);
  * emu_buffer_layout - where to place `nbufs` buffers of `bytes` bytes each
  * inside one device allocation so that HBM serves them evenly: buffer i
  * starts at offsets[i] = i * slot, with slot = bytes rounded up to 64 KiB,
- * plus 4 KiB.  Buffers that a collective reads or writes at the same offset
+ * plus 6 KiB.  Buffers that a collective reads or writes at the same offset
  * (the same element of every rank) then start at different positions
  * modulo 64 KiB instead of the same one.  The allocation needs *pool_bytes
- * bytes and a base aligned to 64 KiB.  Measured on MI355X with the fused
- * all-reduce: 32 ranks x 16 MiB f16 ran at 4.2 TB/s with every buffer at a
- * 16 MiB-aligned slot and at 5.4 TB/s with this layout (16 ranks x 32 MiB
- * bf16: 5.1 -> 5.5 TB/s; 8 ranks x 64 MiB f32: unchanged).  Host arithmetic
- * only; the library works with buffers placed anywhere.
+ * bytes and a base aligned to 64 KiB.  The stagger was chosen on MI355X
+ * for the best worst case over the all-reduce workloads (8 ranks at 16 to
+ * 256 MiB, 15 and 16 ranks bf16, 4 x 8 ranks f16, i64 and f32; ring and
+ * tree, fused and stepwise; two alternating rounds against staggers of 4,
+ * 5 and 7 KiB): no leg below 66.7% of 8 TB/s fused or 62% stepwise, where
+ * 4 KiB let the fused ring at 128 MiB per rank fall to 59% and the 16-rank
+ * stepwise ring to 58%; it costs the 8-rank 64 MiB fused pass about 1%.
+ * Host arithmetic only; the library works with buffers placed anywhere.
  * Errors: EMU_ERR_INVALID_ARGUMENT for nbufs == 0, NULL pointers, or a
  * pool size that does not fit in size_t.
  */

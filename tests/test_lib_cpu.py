@@ -172,14 +172,15 @@ def test_device_transport_init_accepts_ring_with_any_rank_count():
 
 
 def test_buffer_layout():
-    # buffer i at i * slot, slot = bytes rounded up to 64 KiB plus 4 KiB:
-    # consecutive buffers start 4 KiB apart modulo 64 KiB
+    # buffer i at i * slot, slot = bytes rounded up to 64 KiB plus 6 KiB:
+    # consecutive buffers start 6 KiB apart modulo 64 KiB (32 distinct
+    # positions before the pattern repeats)
     for nbufs, nbytes in ((1, 0), (2, 1), (64, 16 << 20), (17, (64 << 10) + 1), (3, 4096)):
         offs, pool = E.buffer_layout(nbufs, nbytes)
-        slot = -(-nbytes // (64 << 10)) * (64 << 10) + 4096
+        slot = -(-nbytes // (64 << 10)) * (64 << 10) + 6144
         assert offs == [i * slot for i in range(nbufs)] and pool == nbufs * slot
         assert all(offs[i] + nbytes <= offs[i + 1] for i in range(nbufs - 1))
-        residues = [o % (64 << 10) for o in offs[:16]]
+        residues = [o % (64 << 10) for o in offs[:32]]
         assert len(set(residues)) == len(residues)
     L = E.lib()
     import ctypes

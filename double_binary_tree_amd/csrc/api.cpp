@@ -412,9 +412,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.627389, 669774}, {0.547849, 682402}}, {{0.192863, 665572}, {0.164171, 813924}}},   // 8 ranks
-    {{{0.653504, 481792}, {1.01233, 341359}}, {{0.129828, 414881}, {0.655643, 447901}}},    // 16 ranks
-    {{{0.689327, 229263}, {0.872081, 175906}}, {{0.0806491, 198835}, {0.414628, 218616}}},  // 32 ranks
+    {{{0.629603, 677636}, {0.54866, 680661}}, {{0.192997, 669520}, {0.164835, 831157}}},    // 8 ranks
+    {{{0.654176, 490007}, {1.01558, 347495}}, {{0.131385, 413431}, {0.655484, 452045}}},    // 16 ranks
+    {{{0.687934, 229801}, {0.867329, 173762}}, {{0.0778968, 197511}, {0.402749, 218205}}},  // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

@@ -33,13 +33,15 @@ constexpr int kFusedThreads = EMU_FUSED_THREADS;
 #ifndef EMU_FUSED_VPT
 #define EMU_FUSED_VPT 1
 #endif
-#ifndef EMU_FUSED_BATCH
-#define EMU_FUSED_BATCH 8
-#endif
 constexpr int kVpt = EMU_FUSED_VPT;      // vectors per lane in a full tile
 constexpr uint32_t kXcds = 8;            // accelerator complex dies of the chip
-constexpr int kBatch = EMU_FUSED_BATCH;  // ranks whose loads are issued back to back
-static_assert(kBatch >= 4, "the remainder of a batch is folded 4, 2 and 1 inputs at a time");
+// Ranks whose loads a lane issues back to back before the first fold, a
+// launch-time choice: 8 below 16 ranks, 16 from 16 ranks up.  Measured on
+// MI355X (3 alternating rounds): 16 at 16 and 32 ranks ran 0.4-2.5% faster
+// on the 16- and 32-rank workloads than 8 (f32 max within 0.3%), 32 was
+// 1-4% slower on the tree programs; below 16 ranks the batch of 8 keeps
+// the kernel at 44-48 VGPRs.
+constexpr int kBatchSmall = 8, kBatchLarge = 16;
 
 // The register stack is indexed with the (wave-uniform) level of the
 // program; the compiler keeps it in VGPRs and indexes it relatively.
@@ -117,7 +119,7 @@ __device__ __forceinline__ void fold_batch(const FusedArgs& a, const uint32_t* _
 }
 
 // Evaluate V whole-vector positions.
-template <typename R, int MODE, int V>
+template <typename R, int MODE, int V, int B>
 __device__ __forceinline__ void evaluate(const FusedArgs& a, const uint32_t* __restrict__ rows, uint32_t variant,
                                          uint64_t boff, uint32_t stride, u32x4 (&out)[V]) {
   const uint32_t n = a.nranks;
@@ -126,7 +128,10 @@ __device__ __forceinline__ void evaluate(const FusedArgs& a, const uint32_t* __r
 #pragma unroll
   for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
   uint32_t j = 0;
-  for (; j + kBatch <= n; j += kBatch) fold_batch<R, MODE, V, kBatch>(a, rows, variant, j, boff, stride, acc, g);
+  static_assert(B == 8 || B == 16, "the remainder of a batch is folded 8, 4, 2 and 1 inputs at a time");
+  for (; j + B <= n; j += B) fold_batch<R, MODE, V, B>(a, rows, variant, j, boff, stride, acc, g);
+  if constexpr (B > 8)
+    for (; j + 8 <= n; j += 8) fold_batch<R, MODE, V, 8>(a, rows, variant, j, boff, stride, acc, g);
   for (; j + 4 <= n; j += 4) fold_batch<R, MODE, V, 4>(a, rows, variant, j, boff, stride, acc, g);
   if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, rows, variant, j, boff, stride, acc, g); j += 2; }
   if (j < n) fold_batch<R, MODE, V, 1>(a, rows, variant, j, boff, stride, acc, g);
@@ -166,21 +171,10 @@ __device__ __forceinline__ void partial_vector(const FusedArgs& a, const uint32_
 }
 
 // Write V results to every rank.
-#ifndef EMU_STORE_GROUPS
-#define EMU_STORE_GROUPS 0
-#endif
 template <int V>
 __device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, uint32_t stride, const u32x4 (&res)[V]) {
   const uint32_t n = a.nranks;
   uint32_t r = 0;
-#if EMU_STORE_GROUPS
-  for (; r + kBatch <= n; r += kBatch) {
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-#pragma unroll
-      for (int v = 0; v < V; ++v) st_vec(a.recv[r + i], boff + (uint64_t)v * stride, res[v]);
-  }
-#endif
   for (; r < n; ++r)
 #pragma unroll
     for (int v = 0; v < V; ++v) st_vec(a.recv[r], boff + (uint64_t)v * stride, res[v]);
@@ -191,7 +185,7 @@ __device__ __forceinline__ void store_all(const FusedArgs& a, uint64_t boff, uin
 // reduce-scatter folds the same way and writes only the block owner's
 // output, one block lower; all-gather copies the block owner's input (one
 // block lower) to every rank's output.
-template <typename R, int MODE, int COLL, int V>
+template <typename R, int MODE, int COLL, int V, int B>
 __device__ __forceinline__ void do_positions(const FusedArgs& a, const uint32_t* __restrict__ rows,
                                              uint32_t variant, uint64_t boff, uint32_t stride) {
   const uint32_t owner = variant >> 16;
@@ -203,7 +197,7 @@ __device__ __forceinline__ void do_positions(const FusedArgs& a, const uint32_t*
     store_all<V>(a, boff, stride, x);
   } else {
     u32x4 res[V];
-    evaluate<R, MODE, V>(a, rows, variant, boff, stride, res);
+    evaluate<R, MODE, V, B>(a, rows, variant, boff, stride, res);
     if constexpr (COLL == kReduceScatter) {
 #pragma unroll
       for (int v = 0; v < V; ++v) st_vec(a.recv[owner], boff - shift + (uint64_t)v * stride, res[v]);
@@ -220,7 +214,7 @@ __device__ __forceinline__ void do_positions(const FusedArgs& a, const uint32_t*
 // output positions (all-gather): the side with N accesses per position.
 // The tile table and the order rows come as their own read-only arguments
 // so that the (uniform) loads from them go through the scalar unit.
-template <typename R, int MODE, int ESZ, int COLL>
+template <typename R, int MODE, int ESZ, int COLL, int B>
 __global__ __launch_bounds__(kFusedThreads) void fused_collective(const FusedArgs a, const Tile* __restrict__ tiles,
                                                                   const uint32_t* __restrict__ rows) {
   constexpr uint32_t unit = kVecBytes / ESZ;
@@ -239,9 +233,9 @@ __global__ __launch_bounds__(kFusedThreads) void fused_collective(const FusedArg
         // The register stack is indexed dynamically; one position at a time
         // keeps it in VGPRs.
         for (int v = 0; v < kVpt; ++v)
-          do_positions<R, MODE, COLL, 1>(a, rows, tile.variant, base + lane_off + (uint64_t)v * stride, 0);
+          do_positions<R, MODE, COLL, 1, B>(a, rows, tile.variant, base + lane_off + (uint64_t)v * stride, 0);
       } else {
-        do_positions<R, MODE, COLL, kVpt>(a, rows, tile.variant, base + lane_off, stride);
+        do_positions<R, MODE, COLL, kVpt, B>(a, rows, tile.variant, base + lane_off, stride);
       }
       continue;
     }
@@ -255,19 +249,29 @@ __global__ __launch_bounds__(kFusedThreads) void fused_collective(const FusedArg
       if (pos < tile.start || pos >= end) continue;
       const uint64_t boff = pos * ESZ;
       if (end - pos >= unit)
-        do_positions<R, MODE, COLL, 1>(a, rows, tile.variant, boff, 0);
+        do_positions<R, MODE, COLL, 1, B>(a, rows, tile.variant, boff, 0);
       else
         partial_vector<R, MODE, COLL>(a, rows, tile.variant, boff, (int)((end - pos) * ESZ));
     }
   }
 }
 
+template <DType T, Op O, int MODE, int COLL, int B = kBatchSmall>
+static hipError_t launch_b(const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL((fused_collective<Red<T, O>, MODE, Unit<T>::esz, COLL, B>), dim3(grid), dim3(kFusedThreads),
+                     0, stream, a, tiles, rows);
+  return hipGetLastError();
+}
+
+// The load batch by rank count (the all-gather is a copy: one load per lane).
 template <DType T, Op O, int MODE, int COLL>
 static hipError_t launch_one(const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
                              hipStream_t stream) {
-  hipLaunchKernelGGL((fused_collective<Red<T, O>, MODE, Unit<T>::esz, COLL>), dim3(grid), dim3(kFusedThreads),
-                     0, stream, a, tiles, rows);
-  return hipGetLastError();
+  if constexpr (COLL != kAllGather) {
+    if (a.nranks >= 16) return launch_b<T, O, MODE, COLL, kBatchLarge>(a, tiles, rows, grid, stream);
+  }
+  return launch_b<T, O, MODE, COLL>(a, tiles, rows, grid, stream);
 }
 
 template <DType T, Op O>

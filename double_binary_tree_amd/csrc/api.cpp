@@ -376,12 +376,28 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     const int occ_t = p->ll ? ll_occupancy(false, t, op, p->block, p->lds)
                             : stepwise_occupancy(false, t, op, p->block, p->lds, p->group);
     const long per_cu = env_long("EMU_TREE_TASKS_PER_CU", occ_t);
-    std::vector<TreeTask> tasks;
-    std::vector<TreeNode> nodes;
-    build_tree_tasks(c.topo, count, unit, slice_elems, (uint64_t)cus * per_cu, &tasks, &nodes);
-    p->ntasks = (uint32_t)tasks.size();
     uint32_t h = 0;
     for (const auto& ch : c.topo.channels) h = std::max<uint32_t>(h, (uint32_t)ch.height);
+    // Pieces of at least min_piece * H slices, as long as the message still
+    // gives every CU a piece.  A piece pays 2H stages of fill and drain, and
+    // one piece per resident workgroup leaves a small message's pieces a
+    // slice or two each, so nearly every stage is fill or drain while eight
+    // waves per SIMD contend to issue each stage's scalar-heavy control.
+    // Measured on MI355X (slot protocol, one rank per wave; 2 alternating
+    // rounds): pieces of at least H slices ran 8 ranks x 1 / 2 / 4 MiB in
+    // 11.6 / 16.3 / 20.9 us instead of 17.7 / 19.8 / 22.0 (16 ranks x 1 MiB:
+    // 12.3 against 19.0 us) and left 8 MiB and up unchanged; 2H and longer
+    // were slower, as was any minimum with two ranks per wave (17-32 ranks)
+    // or below one slice per CU.  Debug knob EMU_TREE_PIECE_MIN.
+    const long min_piece = env_count("EMU_TREE_PIECE_MIN", !p->ll && p->group == 64 ? 1 : 0);
+    const uint64_t cells = (count + slice_elems - 1) / slice_elems;
+    const uint64_t min_cells =
+        min_piece > 0 ? std::min<uint64_t>((uint64_t)min_piece * std::max<uint32_t>(h, 1), (cells + cus - 1) / cus)
+                      : 1;
+    std::vector<TreeTask> tasks;
+    std::vector<TreeNode> nodes;
+    build_tree_tasks(c.topo, count, unit, slice_elems, (uint64_t)cus * per_cu, &tasks, &nodes, min_cells);
+    p->ntasks = (uint32_t)tasks.size();
     p->height = h;
     p->keep(kTasks, tasks);
     p->keep(kTable, nodes);
@@ -412,8 +428,8 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.629603, 677636}, {0.54866, 680661}}, {{0.192997, 669520}, {0.164835, 831157}}},    // 8 ranks
-    {{{0.654176, 490007}, {1.01558, 347495}}, {{0.131385, 413431}, {0.655484, 452045}}},    // 16 ranks
+    {{{0.630524, 678011}, {0.536757, 698926}}, {{0.192654, 668631}, {0.164691, 825607}}},   // 8 ranks
+    {{{0.65397, 488211}, {0.992067, 365160}}, {{0.123766, 421070}, {0.650964, 461749}}},    // 16 ranks
     {{{0.687934, 229801}, {0.867329, 173762}}, {{0.0778968, 197511}, {0.402749, 218205}}},  // 32 ranks
 };
 

@@ -47,3 +47,16 @@ def test_sweep_largest_message_every_element(nch, algo):
     from dataclasses import replace
     w = replace(I.WORKLOADS["sweep8_f32"], nchannels=nch, count=1 << 26)
     check_every_element(w, algo, inplace_modes=(False,))
+
+
+@pytest.mark.parametrize("name,count", [("chain8_f32", (1 << 18) + 37), ("chain8_f32", (1 << 19) + 4099),
+                                        ("dtree16_bf16", (1 << 19) + 11), ("dtree15_bf16", (3 << 18) + 5)])
+def test_mid_size_tree_pieces_every_element(name, count):
+    """Messages of 1-2 MiB per rank with a ragged tail, where the stepwise
+    tree's pieces hold several slices each (at least min(H, slices per CU)
+    rather than one piece per resident workgroup): ring and tree, fused and
+    stepwise, every element against the oracle."""
+    from dataclasses import replace
+    w = replace(I.WORKLOADS[name], count=count)
+    for algo in ("tree", "ring"):
+        check_every_element(w, algo, inplace_modes=(False,))

@@ -378,7 +378,7 @@ std::vector<uint32_t> ring_channel_loops(const Topology& topo, uint64_t count, u
 
 void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t slice_elems,
                       uint64_t target_tasks, std::vector<TreeTask>* tasks,
-                      std::vector<TreeNode>* nodes) {
+                      std::vector<TreeNode>* nodes, uint64_t min_cells) {
   tasks->clear();
   const std::vector<Range> chans = channel_ranges(count, unit, topo.nchannels);
   // Adjacent channels with the same tree records are contiguous ranges of
@@ -402,7 +402,7 @@ void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint6
   if (target_tasks == 0) target_tasks = 1;
   // Cells per task: even split of all cells, and few enough elements that a
   // task's length fits the 32-bit field.
-  uint64_t per_task = std::max<uint64_t>(1, ceil_div(total_cells, target_tasks));
+  uint64_t per_task = std::max<uint64_t>(std::max<uint64_t>(1, min_cells), ceil_div(total_cells, target_tasks));
   per_task = std::min<uint64_t>(per_task, ((uint64_t)1 << 31) / slice_elems);
   for (const Seg& g : segs) {
     uint64_t pos = g.start;

@@ -75,9 +75,11 @@ std::vector<uint32_t> ring_channel_loops(const Topology& topo, uint64_t count, u
 
 // Stepwise tree: about target_tasks contiguous pieces of the message, each
 // inside one run of channels with the same tree records and cut at
-// slice-cell boundaries, and the per-(channel, rank) tree table.
+// slice-cell boundaries, and the per-(channel, rank) tree table.  Pieces
+// hold at least min_cells slice cells where the segments allow (fewer,
+// longer pieces).
 void build_tree_tasks(const Topology& topo, uint64_t count, uint64_t unit, uint64_t slice_elems,
                       uint64_t target_tasks, std::vector<TreeTask>* tasks,
-                      std::vector<TreeNode>* nodes);
+                      std::vector<TreeNode>* nodes, uint64_t min_cells = 1);
 
 }  // namespace emu

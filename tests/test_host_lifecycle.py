@@ -34,8 +34,9 @@ def test_lifecycle_under_sanitizers():
            "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include", "-I" + CSRC, "-I" + os.path.join(ROOT, "include"),
            "-I" + HOST, os.path.join(HOST, "lifecycle_check.cpp"), os.path.join(HOST, "fake_hip.cpp"),
            os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "topology.cpp"),
-           "-o", exe]
+           "-o", exe + f".{os.getpid()}"]
     subprocess.run(cmd, check=True, capture_output=True)
+    os.replace(exe + f".{os.getpid()}", exe)   # atomic: parallel workers may run the previous build
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1")
     env.pop("EMU_DEBUG", None)
     out = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)

@@ -32,8 +32,9 @@ def dump():
     os.makedirs(BUILD, exist_ok=True)
     cmd = [gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I" + CSRC, os.path.join(ROOT, "tests", "host", "planner_dump.cpp"),
-           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "topology.cpp"), "-o", EXE]
+           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "topology.cpp"), "-o", EXE + f".{os.getpid()}"]
     subprocess.run(cmd, check=True, capture_output=True)
+    os.replace(EXE + f".{os.getpid()}", EXE)   # atomic: parallel workers may run the previous build
     cache = {}
 
     def run(n, m, nch, chunk_bytes, esz, count, pattern=0, intra=None):

@@ -36,11 +36,13 @@ constexpr int kFusedThreads = EMU_FUSED_THREADS;
 constexpr int kVpt = EMU_FUSED_VPT;      // vectors per lane in a full tile
 constexpr uint32_t kXcds = 8;            // accelerator complex dies of the chip
 // Ranks whose loads a lane issues back to back before the first fold, a
-// launch-time choice: 8 below 16 ranks, 16 from 16 ranks up.  Measured on
-// MI355X (3 alternating rounds): 16 at 16 and 32 ranks ran 0.4-2.5% faster
-// on the 16- and 32-rank workloads than 8 (f32 max within 0.3%), 32 was
-// 1-4% slower on the tree programs; below 16 ranks the batch of 8 keeps
-// the kernel at 44-48 VGPRs.
+// launch-time choice: 8 up to 8 ranks, 16 above.  With 16, the ranks past
+// the last whole batch are folded in one more phase (fold_rest).  Measured
+// on MI355X (3 alternating rounds): 16 at 16 and 32 ranks ran 0.4-2.5%
+// faster on the 16- and 32-rank workloads than 8 (f32 max within 0.3%), 32
+// was 1-4% slower on the tree programs; at 15 ranks one phase of 15 loads
+// ran 3.1% faster than phases of 8, 4, 2 and 1 (tree, 32 MiB bf16; ring
+// 1.5%).  Up to 8 ranks the batch of 8 keeps the kernel at 44-48 VGPRs.
 constexpr int kBatchSmall = 8, kBatchLarge = 16;
 
 // The register stack is indexed with the (wave-uniform) level of the
@@ -118,6 +120,40 @@ __device__ __forceinline__ void fold_batch(const FusedArgs& a, const uint32_t* _
   for (int i = 0; i < B; ++i) consume<R, MODE, V>(e[i], j + i, x[i], acc, g);
 }
 
+// Fold the last r (1 <= r < B) inputs j .. j+r-1 in one phase: B loads
+// issued back to back before the first fold, of which entries r .. B-1 pass
+// an out-of-range offset to a raw buffer view (the hardware returns zeros
+// without a memory access) and are not folded.  So a rank count that is not
+// a multiple of the batch costs one memory round trip more, not one per
+// power of two in its remainder; and no load sits under a branch (the
+// merges would copy every loaded register).  The views are based at the
+// first active lane's offset (uniform); every lane's offset lies at or
+// above it, within the tile.
+template <typename R, int MODE, int V, int B>
+__device__ __forceinline__ void fold_rest(const FusedArgs& a, const uint32_t* __restrict__ rows, uint32_t variant,
+                                          uint32_t j, uint32_t r, uint64_t boff, uint32_t stride, u32x4 (&acc)[V],
+                                          u32x4 (&g)[stack_regs<MODE>()]) {
+  const uint64_t wbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(boff >> 32)) << 32) |
+                         (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)boff);
+  const uint32_t loff = (uint32_t)(boff - wbase);
+  uint32_t e[B];
+  u32x4 x[B][V];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    const bool live = (uint32_t)i < r;
+    e[i] = order_entry<MODE>(a, rows, variant, j + (live ? (uint32_t)i : 0u));
+    const auto rs = buffer_view(static_cast<const char*>(a.send[e[i] & 0xFF]) + wbase);
+#pragma unroll
+    for (int v = 0; v < V; ++v) x[i][v] = ld_buf(rs, live ? loff + (uint32_t)v * stride : kNoLoad);
+  }
+#if EMU_SCHED_BARRIER
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+#pragma unroll
+  for (int i = 0; i < B; ++i)
+    if ((uint32_t)i < r) consume<R, MODE, V>(e[i], j + i, x[i], acc, g);
+}
+
 // Evaluate V whole-vector positions.
 template <typename R, int MODE, int V, int B>
 __device__ __forceinline__ void evaluate(const FusedArgs& a, const uint32_t* __restrict__ rows, uint32_t variant,
@@ -128,13 +164,18 @@ __device__ __forceinline__ void evaluate(const FusedArgs& a, const uint32_t* __r
 #pragma unroll
   for (int i = 0; i < stack_regs<MODE>(); ++i) g[i] = u32x4{0, 0, 0, 0};
   uint32_t j = 0;
-  static_assert(B == 8 || B == 16, "the remainder of a batch is folded 8, 4, 2 and 1 inputs at a time");
+  static_assert(B == kBatchSmall || B == kBatchLarge, "the load batch is 8 or 16");
   for (; j + B <= n; j += B) fold_batch<R, MODE, V, B>(a, rows, variant, j, boff, stride, acc, g);
-  if constexpr (B > 8)
-    for (; j + 8 <= n; j += 8) fold_batch<R, MODE, V, 8>(a, rows, variant, j, boff, stride, acc, g);
-  for (; j + 4 <= n; j += 4) fold_batch<R, MODE, V, 4>(a, rows, variant, j, boff, stride, acc, g);
-  if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, rows, variant, j, boff, stride, acc, g); j += 2; }
-  if (j < n) fold_batch<R, MODE, V, 1>(a, rows, variant, j, boff, stride, acc, g);
+  if constexpr (B == kBatchLarge) {
+    if (j < n) fold_rest<R, MODE, V, B>(a, rows, variant, j, n - j, boff, stride, acc, g);
+  } else {
+    // Up to 8 ranks the remainder (below 8 ranks only) is folded 4, 2 and 1
+    // inputs at a time: the one-phase remainder shifted the 8-rank kernel's
+    // code and measured 0.8% slower there.
+    for (; j + 4 <= n; j += 4) fold_batch<R, MODE, V, 4>(a, rows, variant, j, boff, stride, acc, g);
+    if (j + 2 <= n) { fold_batch<R, MODE, V, 2>(a, rows, variant, j, boff, stride, acc, g); j += 2; }
+    if (j < n) fold_batch<R, MODE, V, 1>(a, rows, variant, j, boff, stride, acc, g);
+  }
 #pragma unroll
   for (int v = 0; v < V; ++v) out[v] = R::post(MODE == kProgram ? g[0] : acc[v]);
 }
@@ -269,7 +310,7 @@ template <DType T, Op O, int MODE, int COLL>
 static hipError_t launch_one(const FusedArgs& a, const Tile* tiles, const uint32_t* rows, int grid,
                              hipStream_t stream) {
   if constexpr (COLL != kAllGather) {
-    if (a.nranks >= 16) return launch_b<T, O, MODE, COLL, kBatchLarge>(a, tiles, rows, grid, stream);
+    if (a.nranks > kBatchSmall) return launch_b<T, O, MODE, COLL, kBatchLarge>(a, tiles, rows, grid, stream);
   }
   return launch_b<T, O, MODE, COLL>(a, tiles, rows, grid, stream);
 }

@@ -483,26 +483,42 @@ __global__ __launch_bounds__(1024) EMU_TREE_OCCUPANCY void step_tree(const StepA
     };
     auto boff_of = [&](int q, int v) -> uint64_t { return pos_of(q, v) * ESZ; };
     // Every slice but the first and the last lies inside the task: each lane
-    // holds a whole vector there, so a store needs no per-lane bounds.  (The
-    // same shortcut for the loads was slower on small messages: the loads'
-    // offsets are a select already, and the branch only lengthens a stage.)
-    auto interior = [&](int q) { return q > 0 && q + 1 < nslices; };
+    // holds a whole vector there, so a store needs no per-lane bounds.
+    // (Range checks compare as unsigned: one compare for both bounds.)
+    auto interior = [&](int q) { return (uint32_t)(q - 1) < (uint32_t)(nslices - 2); };
     // Own input of the wave's ranks for stage st + kPrefetch (rank k reduces
     // slice st - lag_k there): one buffer load per rank, based at its
-    // slice's cell (uniform; computed from uniform values only, so that the
-    // view sits in scalar registers); whole vectors only, a partial vector
-    // at the task end is read when it is consumed (fix_slice).
+    // slice's cell (uniform: a running base per rank that moves one slice on
+    // at every stage, so that the view sits in scalar registers without a
+    // 64-bit product per stage); whole vectors only, a partial vector at the
+    // task end is read when it is consumed (fix_slice).  A base outside the
+    // buffer is never used: the range check is on the offset, and every lane
+    // without a slice passes kNoLoad.  (Offsets for the first and the last
+    // slice computed once per task instead of per stage took a fifth off a
+    // stage at small sizes too, but with the running base made the 8-rank
+    // chain 6-10% slower from 16 MiB per rank up; either change alone did not.)
+    const uint64_t slice_bytes = (uint64_t)slice_elems * ESZ;
+    uint32_t lane_off[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) lane_off[v] = (uint32_t)((v * g + p) * kVecBytes);
+    // The view base of rank k's last load: the first call (stage 0, slice
+    // -lag_k) moves it one slice on before use.  Wraps as unsigned, like
+    // the slice index it follows.
+    uint64_t lbase[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k)
+      lbase[k] = (uint64_t)wsrc[k] + (first_cell - (uint64_t)(int64_t)(lag_k[k] + 1)) * slice_bytes;
     auto load_stage = [&](int st, u32x4 (&x)[RPW][V]) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const int qk = st - lag_k[k];
-        const bool en = live_k[k] && qk >= 0 && qk < nslices;
-        const auto rs = buffer_view(wsrc[k] + (first_cell + (uint64_t)(en ? qk : 0)) * slice_elems * ESZ);
+        const bool en = live_k[k] && (uint32_t)qk < (uint32_t)nslices;
+        lbase[k] += slice_bytes;
+        const auto rs = buffer_view(reinterpret_cast<const void*>(lbase[k]));
+        const bool mine = RPW == 1 || grp == (uint32_t)k;
 #pragma unroll
         for (int v = 0; v < V; ++v) {
-          const uint32_t lane = (uint32_t)((v * g + p) * kVecBytes);
-          const bool mine = RPW == 1 || grp == (uint32_t)k;
-          x[k][v] = ld_buf(rs, en && mine && nbytes_of(qk, v) == kVecBytes ? lane : kNoLoad);
+          x[k][v] = ld_buf(rs, en && mine && nbytes_of(qk, v) == kVecBytes ? lane_off[v] : kNoLoad);
         }
       }
     };
@@ -545,10 +561,12 @@ __global__ __launch_bounds__(1024) EMU_TREE_OCCUPANCY void step_tree(const StepA
 #pragma unroll
       for (int i = 0; i < kPrefetch; ++i) {
         const int st = st0 + i;
-        const bool live = st >= 0 && st < nstages;
+        const bool live = (uint32_t)st < (uint32_t)nstages;
         const int cur = st & 1, prv = cur ^ 1;
         const int qu = st - up_lag;
-        if (live && active && qu >= 0 && qu < nslices) {
+        // (outside stages 0 .. nstages-1 both slice indices are out of range:
+        // 0 <= depth <= H)
+        if (active && (uint32_t)qu < (uint32_t)nslices) {
           u32x4 acc[V];
 #pragma unroll
           for (int v = 0; v < V; ++v) {
@@ -581,7 +599,7 @@ __global__ __launch_bounds__(1024) EMU_TREE_OCCUPANCY void step_tree(const StepA
         load_stage(st + kPrefetch, q[i]);
         if (live) {
           const int qd = st - dn_lag;
-          if (active && !is_root && qd >= 0 && qd < nslices) {
+          if (active && !is_root && (uint32_t)qd < (uint32_t)nslices) {
             u32x4 x[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) x[v] = dn_slot(prv, (uint32_t)me.up, v);

@@ -208,17 +208,17 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
     // its [start, end) range.  view_u: for a wave-uniform b, in scalar
     // registers; view_of: for the lane's own block.
     struct View { uint64_t cell, start, end; };
-    auto view_u = [&](uint32_t b) -> View {
-      const RingLoopBlock d = blk[b];
+    auto view_u_of = [&](const RingLoopBlock& d) -> View {
       const uint64_t start = wave_u64<true>(d.offset);
       const uint32_t nelem = wave_u32<true>(d.nelem), cell = wave_u32<true>(d.first_cell);
       return {(uint64_t)cell * slice_elems, start, start + nelem};
     };
-    auto view_of = [&](uint32_t b) -> View {
-      if constexpr (WAVE) return view_u(b);
-      const RingLoopBlock d = blk[b];
+    auto view_u = [&](uint32_t b) -> View { return view_u_of(blk[b]); };
+    auto view_from = [&](const RingLoopBlock& d) -> View {
+      if constexpr (WAVE) return view_u_of(d);
       return {(uint64_t)d.first_cell * slice_elems, d.offset, d.offset + d.nelem};
     };
+    auto view_of = [&](uint32_t b) -> View { return view_from(blk[b]); };
     // A cell that lies wholly inside its block: every lane holds a whole
     // vector, so no lane needs its bounds checked.
     auto whole = [&](const View& w) { return w.start <= w.cell && w.cell + slice_elems <= w.end; };
@@ -234,11 +234,12 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
     // partial vector at the message end is read when it is consumed
     // (fix_block).  Issued for the whole wave, outside any per-lane branch,
     // and never into a register that anything but a load writes.
-    auto load_blocks = [&](const uint32_t (&bk)[RPW], u32x4 (&x)[RPW][V], bool enable) {
+    auto load_blocks = [&](const uint32_t (&bk)[RPW], u32x4 (&x)[RPW][V], bool enable, View* w0 = nullptr) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) {
         const bool en = enable && wave * RPW + k < n;
         const View w = view_u(bk[k]);
+        if (k == 0 && w0) *w0 = w;
         const auto rs = buffer_view(wsrc[k] + (w.cell * ESZ - wshift[k]));
         const bool mine = WAVE || grp == (uint32_t)k;
         if (en && whole(w)) {
@@ -261,8 +262,7 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
         for (int k = 1; k < RPW; ++k) out[v] |= x[k][v];
       }
     };
-    auto fix_block = [&](uint32_t b, u32x4 (&x)[V]) {
-      const View w = view_of(b);
+    auto fix_view = [&](const View& w, u32x4 (&x)[V]) {
       if (w.cell + slice_elems <= w.end) return;   // a partial vector can only sit at the block end
 #pragma unroll
       for (int v = 0; v < V; ++v) {
@@ -271,8 +271,8 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
         if (nb > 0 && nb < kVecBytes) x[v] = ld_part(src_me, pos * ESZ - load_shift, nb);
       }
     };
-    auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) {
-      const View w = view_of(b);
+    auto fix_block = [&](uint32_t b, u32x4 (&x)[V]) { fix_view(view_of(b), x); };
+    auto store_view = [&](const View& w, const u32x4 (&x)[V]) {
       if (whole(w)) {
 #pragma unroll
         for (int v = 0; v < V; ++v)
@@ -286,6 +286,7 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
         if (nb) st_any(dst_me, pos * ESZ - store_shift, nb, R::post(x[v]));
       }
     };
+    auto store_block = [&](uint32_t b, const u32x4 (&x)[V]) { store_view(view_of(b), x); };
     // the positions of the wave, for block indices counted per position
     uint32_t pos_k[RPW];
 #pragma unroll
@@ -329,21 +330,25 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
     // step 0: send own block r; the blocks of steps 1..PF are loaded ahead
     // (queue q[0] is the next step's block).  Block of step s at position
     // k: (k - s) mod N, counted down per position.
+    // With one rank per wave the block's view (read from LDS to place its
+    // load) rides in the queue beside the data, so the step that consumes
+    // the block reads no descriptor again.
     u32x4 own[RPW][V], q[kPrefetch][RPW][V];
+    View own_v, qv[kPrefetch];
     uint32_t bpf[RPW];
-    load_blocks(pos_k, own, true);
+    load_blocks(pos_k, own, true, &own_v);
 #pragma unroll
     for (int k = 0; k < RPW; ++k) bpf[k] = pos_k[k];
 #pragma unroll
     for (int i = 0; i < kPrefetch; ++i) {
 #pragma unroll
       for (int k = 0; k < RPW; ++k) bpf[k] = bpf[k] == 0 ? n - 1 : bpf[k] - 1;
-      load_blocks(bpf, q[i], (uint32_t)i + 1 < n);
+      load_blocks(bpf, q[i], (uint32_t)i + 1 < n, &qv[i]);
     }
     if (active) {
       u32x4 mine[V];
       take(own, mine);
-      fix_block(r, mine);
+      if constexpr (WAVE) fix_view(own_v, mine); else fix_block(r, mine);
 #pragma unroll
       for (int v = 0; v < V; ++v) slot(0, r, v) = R::pre(mine[v]);
     }
@@ -354,23 +359,28 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
       b = b == 0 ? n - 1 : b - 1;
       u32x4 mine[V];
       take(q[0], mine);   // this step's entry (waits for its loads only)
+      const View wb = qv[0];   // the view of block b (one rank per wave)
 #pragma unroll
-      for (int i = 0; i + 1 < kPrefetch; ++i)
+      for (int i = 0; i + 1 < kPrefetch; ++i) {
+        qv[i] = qv[i + 1];
 #pragma unroll
         for (int k = 0; k < RPW; ++k)
 #pragma unroll
           for (int v = 0; v < V; ++v) q[i][k][v] = q[i + 1][k][v];
+      }
       if (s + kPrefetch < n) {
 #pragma unroll
         for (int k = 0; k < RPW; ++k) bpf[k] = bpf[k] == 0 ? n - 1 : bpf[k] - 1;
-        load_blocks(bpf, q[kPrefetch - 1], true);
+        load_blocks(bpf, q[kPrefetch - 1], true, &qv[kPrefetch - 1]);
       }
       if (active) {
-        fix_block(b, mine);
+        if constexpr (WAVE) fix_view(wb, mine); else fix_block(b, mine);
         u32x4 res[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) res[v] = R::op(R::pre(mine[v]), slot((s - 1) & 1, prev, v));
-        if (s == n - 1) store_block(b, res);
+        if (s == n - 1) {
+          if constexpr (WAVE) store_view(wb, res); else store_block(b, res);
+        }
 #pragma unroll
         for (int v = 0; v < V; ++v) slot(s & 1, r, v) = res[v];
       }
@@ -378,16 +388,24 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
     }
     }
     if (COLL == kReduceScatter) continue;
-    // all-gather steps 1..N-1: block (r + 1 - j) mod N, counted down
+    // all-gather steps 1..N-1: block (r + 1 - j) mod N, counted down.  The
+    // descriptor of the next step's block is read from LDS one step ahead
+    // (the task's descriptor set does not change during the task), so its
+    // latency passes under this step's work and barrier.
     uint32_t bg = (r + 1) % n;
+    bg = bg == 0 ? n - 1 : bg - 1;   // step 1's block
+    RingLoopBlock dn = blk[bg];
     for (uint32_t j = 1; j < n; ++j) {
-      bg = bg == 0 ? n - 1 : bg - 1;
-      const uint32_t b = bg;
+      const RingLoopBlock d = dn;
+      if (j + 1 < n) {
+        bg = bg == 0 ? n - 1 : bg - 1;
+        dn = blk[bg];
+      }
       if (active) {
         u32x4 x[V];
 #pragma unroll
         for (int v = 0; v < V; ++v) x[v] = slot((n - 2 + j) & 1, prev, v);
-        store_block(b, x);
+        store_view(view_from(d), x);
         if (j + 1 < n) {
 #pragma unroll
           for (int v = 0; v < V; ++v) slot((n - 1 + j) & 1, r, v) = x[v];

@@ -428,9 +428,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.630524, 678011}, {0.536757, 698926}}, {{0.192654, 668631}, {0.164691, 825607}}},   // 8 ranks
-    {{{0.65397, 488211}, {0.992067, 365160}}, {{0.123766, 421070}, {0.650964, 461749}}},    // 16 ranks
-    {{{0.687934, 229801}, {0.867329, 173762}}, {{0.0778968, 197511}, {0.402749, 218205}}},  // 32 ranks
+    {{{0.594198, 666587}, {0.471077, 697668}}, {{0.193347, 669584}, {0.164199, 828642}}},   // 8 ranks
+    {{{0.625648, 473161}, {0.842188, 392477}}, {{0.122453, 421820}, {0.645906, 459550}}},   // 16 ranks
+    {{{0.649538, 232806}, {0.689637, 175148}}, {{0.0677596, 196264}, {0.384865, 217658}}},  // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

@@ -172,15 +172,18 @@ def _main() -> int:
     if jl:
         jl.close()
     if args.out:
-        write_report(args.out, rows, w)
+        extra = "".join(f" --{k.replace('_', '-')} {v}" for k, v in
+                        (("channels", args.channels), ("min_pow", args.min_pow), ("max_pow", args.max_pow))
+                        if v is not None and v != ap.get_default(k))
+        write_report(args.out, rows, w, extra)
     return 0
 
 
-def write_report(path, rows, w):
+def write_report(path, rows, w, extra=""):
     n = w.nranks
     lines = [f"# Message-size sweep: ring vs tree, fused vs stepwise ({w.name}: {n} ranks on {w.nnodes} node(s), "
              f"{w.dtype} {w.op}, one MI355X)\n\n",
-             f"Command: `python -m double_binary_tree_amd.sweep --workload {w.name} --out <this file>`. Per-launch "
+             f"Command: `python -m double_binary_tree_amd.sweep --workload {w.name}{extra} --out <this file>`. Per-launch "
              f"time of {GRAPH_LAUNCHES} back-to-back launches replayed from a HIP graph (events around the "
              "replays; buffers resident in HBM at the library's placement; no cache flush between launches, so "
              "sizes whose 2·N·S fits the 256 MB Infinity Cache run partly from cache). busbw = S/t · 2(N−1)/N; "

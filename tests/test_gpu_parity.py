@@ -98,6 +98,20 @@ def test_shapes(n, m, nch, algo, mode):
     _check(w, algo, mode, 6 * 1024 + 13, chunk_bytes=256, inplace=False)
 
 
+@pytest.mark.parametrize("n", list(range(1, 41)))
+@pytest.mark.parametrize("algo,per_node", [("ring", False), ("tree", False), ("tree", True)])
+def test_fused_every_rank_count(n, algo, per_node):
+    """The fused pass loads a lane's inputs in batches (8 up to 8 ranks,
+    else 16) and folds the ranks past the last whole batch in one more
+    phase: every rank count from 1 to 40 covers every remainder of both
+    batches, for the ring and chain folds (one node) and for the
+    register-stack programs of the double tree (one rank per node); ragged
+    count, bf16 so that every hop rounds."""
+    nodes = n if per_node else 1
+    w = I.Workload("ranks", 8, n, nodes, (algo,), 3, 4096, "bf16", "sum", 1, ("normal", 1.0))
+    _check(w, algo, "fused", 3 * 1024 + 11, chunk_bytes=4096, inplace=False, salt=n)
+
+
 @pytest.mark.parametrize("mode", ["fused", "stepwise"])
 def test_count_zero_is_noop(mode):
     import torch

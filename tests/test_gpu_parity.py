@@ -112,6 +112,19 @@ def test_fused_every_rank_count(n, algo, per_node):
     _check(w, algo, "fused", 3 * 1024 + 11, chunk_bytes=4096, inplace=False, salt=n)
 
 
+@pytest.mark.parametrize("n", list(range(1, 41)))
+@pytest.mark.parametrize("algo,per_node", [("ring", False), ("tree", False), ("tree", True)])
+def test_stepwise_every_rank_count(n, algo, per_node):
+    """The stepwise kernels change form with the rank count: one rank per
+    wave up to 16 ranks, two up to 32, four beyond; the ring's load queue
+    runs past the last step below 4 ranks; a chain's depth and a double
+    tree's shape change with every count.  Every count from 1 to 40, ragged
+    count, bf16."""
+    nodes = n if per_node else 1
+    w = I.Workload("ranks", 8, n, nodes, (algo,), 3, 4096, "bf16", "sum", 1, ("normal", 1.0))
+    _check(w, algo, "stepwise", 3 * 1024 + 11, chunk_bytes=4096, inplace=False, salt=n)
+
+
 @pytest.mark.parametrize("mode", ["fused", "stepwise"])
 def test_count_zero_is_noop(mode):
     import torch

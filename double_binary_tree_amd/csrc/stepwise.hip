@@ -73,12 +73,20 @@ __device__ __forceinline__ void step_barrier() {
 #ifndef EMU_RING_VPT
 #define EMU_RING_VPT 1
 #endif
+// The ring's own-input queue is one entry deep: it is refilled in place
+// once the step has used it, so the load for step s + 1 is issued at the end
+// of step s and waited for at the start of step s + 1, its latency under the
+// barrier.  Deeper queues are moved on by register copies, which the
+// compiler makes wait for every load in flight (measured on MI355X against
+// two entries: full-size legs 1-3% faster at 8, 16 and 32 ranks, 16 ranks
+// 3-6% faster up to 1 MiB per rank, 32 ranks 9% faster at 8-16 MiB and 5%
+// slower at 256 KiB-2 MiB).
 #ifndef EMU_RING_PREFETCH
-#define EMU_RING_PREFETCH 2
+#define EMU_RING_PREFETCH 1
 #endif
 
 #ifndef EMU_RING_PREFETCH_WAVE
-#define EMU_RING_PREFETCH_WAVE 2
+#define EMU_RING_PREFETCH_WAVE 1
 #endif
 // All-reduce tasks take slice (q + b * skew) mod (slices of the loop) of
 // block b rather than slice q of every block.  Each block still gets every
@@ -360,19 +368,6 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
       u32x4 mine[V];
       take(q[0], mine);   // this step's entry (waits for its loads only)
       const View wb = qv[0];   // the view of block b (one rank per wave)
-#pragma unroll
-      for (int i = 0; i + 1 < kPrefetch; ++i) {
-        qv[i] = qv[i + 1];
-#pragma unroll
-        for (int k = 0; k < RPW; ++k)
-#pragma unroll
-          for (int v = 0; v < V; ++v) q[i][k][v] = q[i + 1][k][v];
-      }
-      if (s + kPrefetch < n) {
-#pragma unroll
-        for (int k = 0; k < RPW; ++k) bpf[k] = bpf[k] == 0 ? n - 1 : bpf[k] - 1;
-        load_blocks(bpf, q[kPrefetch - 1], true, &qv[kPrefetch - 1]);
-      }
       if (active) {
         if constexpr (WAVE) fix_view(wb, mine); else fix_block(b, mine);
         u32x4 res[V];
@@ -384,6 +379,23 @@ __global__ __launch_bounds__(1024) EMU_RING_OCCUPANCY void step_ring(const StepA
 #pragma unroll
         for (int v = 0; v < V; ++v) slot(s & 1, r, v) = res[v];
       }
+      // The queue moves on after this step's entry is consumed, and its last
+      // entry is refilled unconditionally (a load of nothing past the last
+      // step).  Refilling earlier, or under a condition, leaves the entry's
+      // old value live (or two definitions to merge) where the new load
+      // lands, and the compiler moves the loaded registers into place with
+      // copies that wait for every load in flight before the barrier.
+#pragma unroll
+      for (int i = 0; i + 1 < kPrefetch; ++i) {
+        qv[i] = qv[i + 1];
+#pragma unroll
+        for (int k = 0; k < RPW; ++k)
+#pragma unroll
+          for (int v = 0; v < V; ++v) q[i][k][v] = q[i + 1][k][v];
+      }
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) bpf[k] = bpf[k] == 0 ? n - 1 : bpf[k] - 1;
+      load_blocks(bpf, q[kPrefetch - 1], s + kPrefetch < n, &qv[kPrefetch - 1]);
       step_barrier();
     }
     }

@@ -428,9 +428,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.594198, 666587}, {0.471077, 697668}}, {{0.193347, 669584}, {0.164199, 828642}}},   // 8 ranks
-    {{{0.625648, 473161}, {0.842188, 392477}}, {{0.122453, 421820}, {0.645906, 459550}}},   // 16 ranks
-    {{{0.649538, 232806}, {0.689637, 175148}}, {{0.0677596, 196264}, {0.384865, 217658}}},  // 32 ranks
+    {{{0.591204, 665247}, {0.47125, 697583}}, {{0.19228, 668105}, {0.164335, 828745}}},    // 8 ranks
+    {{{0.600435, 473293}, {0.837997, 393345}}, {{0.122071, 419233}, {0.644142, 458988}}},   // 16 ranks
+    {{{0.657035, 238206}, {0.688296, 175420}}, {{0.0675124, 197025}, {0.384247, 218543}}},  // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

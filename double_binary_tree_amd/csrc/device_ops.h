@@ -176,26 +176,36 @@ __device__ __forceinline__ void st_vec(void* base, uint64_t byte_off, u32x4 v) {
 }
 
 // Partial vector at the very end of a buffer: `nbytes` (< 16, a multiple of
-// 2) valid bytes, read and written 16 bits at a time; the rest is zero.
+// 2) valid bytes, never accessed past nbytes; the rest reads as zero.
 __device__ __forceinline__ u32x4 ld_part(const void* base, uint64_t byte_off, int nbytes) {
-  const uint16_t* p = reinterpret_cast<const uint16_t*>(static_cast<const char*>(base) + byte_off);
-  u32x4 v = {0, 0, 0, 0};
-#pragma unroll 1
-  for (int i = 0; 2 * i < nbytes; ++i) {
-    const uint32_t h = (uint32_t)p[i] << (16 * (i & 1));
-    if (i < 2) v.x |= h;
-    else if (i < 4) v.y |= h;
-    else if (i < 6) v.z |= h;
-    else v.w |= h;
+  // Seven half-word loads at most, each from an address inside the nbytes
+  // (half-word k < nbytes / 2, else half-word 0): none conditional, so all
+  // are issued back to back and combined by selects once they arrive, in
+  // one memory round trip.  (Loads under conditions leave values to merge,
+  // and the merge copies wait for the loads one by one.)
+  const uint16_t* h = reinterpret_cast<const uint16_t*>(static_cast<const char*>(base) + byte_off);
+  const int nh = nbytes / 2;
+  uint32_t x[7];
+#pragma unroll
+  for (int k = 0; k < 7; ++k) x[k] = h[k < nh ? k : 0];
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = 2 * i < nh ? x[2 * i] : 0u;
+    const uint32_t hi = 2 * i + 1 < nh ? x[2 * i + 1] : 0u;
+    w[i] = lo | hi << 16;
   }
-  return v;
+  return u32x4{w[0], w[1], w[2], w[3]};
 }
 __device__ __forceinline__ void st_part(void* base, uint64_t byte_off, int nbytes, u32x4 v) {
-  uint16_t* p = reinterpret_cast<uint16_t*>(static_cast<char*>(base) + byte_off);
-#pragma unroll 1
-  for (int i = 0; 2 * i < nbytes; ++i) {
-    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
-    p[i] = (uint16_t)(w >> (16 * (i & 1)));
+  char* c = static_cast<char*>(base) + byte_off;
+  uint32_t* d = reinterpret_cast<uint32_t*>(c);
+  uint16_t* h = reinterpret_cast<uint16_t*>(c);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (4 * i + 4 <= nbytes) d[i] = w[i];
+    else if (4 * i + 2 <= nbytes) h[2 * i] = (uint16_t)w[i];
   }
 }
 

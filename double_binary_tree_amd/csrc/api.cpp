@@ -428,9 +428,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.591204, 665247}, {0.47125, 697583}}, {{0.19228, 668105}, {0.164335, 828745}}},    // 8 ranks
-    {{{0.600435, 473293}, {0.837997, 393345}}, {{0.122071, 419233}, {0.644142, 458988}}},   // 16 ranks
-    {{{0.657035, 238206}, {0.688296, 175420}}, {{0.0675124, 197025}, {0.384247, 218543}}},  // 32 ranks
+    {{{0.566156, 662830}, {0.447388, 715101}}, {{0.190283, 666783}, {0.164693, 825644}}},   // 8 ranks
+    {{{0.58276, 463972}, {0.818678, 405914}}, {{0.122294, 421278}, {0.630355, 463680}}},    // 16 ranks
+    {{{0.630444, 233494}, {0.705665, 177011}}, {{0.0689347, 196989}, {0.389274, 218333}}},  // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

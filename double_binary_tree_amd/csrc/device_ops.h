@@ -209,10 +209,20 @@ __device__ __forceinline__ void st_part(void* base, uint64_t byte_off, int nbyte
   }
 }
 
-// Load / store `nbytes` of one vector (16 = whole vector).
-__device__ __forceinline__ u32x4 ld_any(const void* base, uint64_t byte_off, int nbytes) {
-  return nbytes == kVecBytes ? ld_vec(base, byte_off) : ld_part(base, byte_off, nbytes);
+// One vector of `nbytes` (0 to 16; 0 reads as zeros) at `base` + `lane_off`,
+// `base` wave-uniform and `lane_off` below kBufRange.  The whole-vector load
+// is issued unconditionally through a raw buffer view (kNoLoad where the
+// vector is not whole) and only a partial vector takes a branch, which keeps
+// the whole-vector value out of any merge: a merge with a value loaded under
+// a condition becomes a register copy that waits for the load, so the caller
+// could no longer overlap the load with what follows it.
+__device__ __forceinline__ u32x4 ld_lane(const void* base, uint32_t lane_off, int nbytes) {
+  u32x4 x = ld_buf(buffer_view(base), nbytes == kVecBytes ? lane_off : kNoLoad);
+  if (nbytes > 0 && nbytes < kVecBytes) x = ld_part(base, lane_off, nbytes);
+  return x;
 }
+
+// Store `nbytes` of one vector (16 = whole vector).
 __device__ __forceinline__ void st_any(void* base, uint64_t byte_off, int nbytes, u32x4 v) {
   if (nbytes == kVecBytes) st_vec(base, byte_off, v);
   else st_part(base, byte_off, nbytes, v);

@@ -170,10 +170,22 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
       const uint64_t left = w.end - w.pos;
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
-    auto load = [&](uint32_t b) -> u32x4 {
+    // Own input of block b: the whole vectors through a raw buffer view,
+    // unconditionally (kNoLoad for a lane without one, or for every lane
+    // when `live` is false), and a partial vector, only ever at a block's
+    // end, by load_part once the value is needed.  Every step then refills
+    // the same registers: a load under a condition would leave two values
+    // to merge, and the merge copy would wait for the load before the step
+    // could wait for its item.
+    auto cell_of = [&](const View& w) { return static_cast<const char*>(a.send[me]) + w.cell * ESZ; };
+    auto load = [&](uint32_t b, bool live) -> u32x4 {
+      const View w = view_of(b);
+      return ld_buf(buffer_view(cell_of(w)), live && nbytes_of(w) == kVecBytes ? p * kVecBytes : kNoLoad);
+    };
+    auto load_part = [&](uint32_t b, u32x4& x) {
       const View w = view_of(b);
       const int nb = nbytes_of(w);
-      return nb ? ld_any(a.send[me], w.pos * ESZ, nb) : u32x4{0, 0, 0, 0};
+      if (nb > 0 && nb < kVecBytes) x = ld_part(cell_of(w), p * kVecBytes, nb);
     };
     auto store = [&](uint32_t b, const u32x4& x) {
       const View w = view_of(b);
@@ -187,7 +199,8 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
     auto send = [&](const u32x4& x) { return ll_send(ctl, my_fifo, &consumed[r], nsent++, p, x); };
     auto recv = [&](u32x4& x) { return ll_recv(ctl, in_fifo, &consumed[prev], nrecv++, p, x); };
 
-    u32x4 own = load(r);
+    u32x4 own = load(r, true);
+    load_part(r, own);
     if (n == 1) {   // one rank: no steps (and no FIFO traffic)
       store(0, R::pre(own));
       continue;
@@ -196,13 +209,14 @@ __global__ __launch_bounds__(1024) void ll_ring(const StepArgs a, const RingTask
     // blocks counted down instead of taken modulo N: step s works on block
     // (r - s) mod N, all-gather step j on (r + 1 - j) mod N
     uint32_t b = r == 0 ? n - 1 : r - 1;
-    own = load(b);   // step 1's own input, read while waiting
+    own = load(b, true);   // step 1's own input, read while waiting
     for (uint32_t s = 1; s < n; ++s) {
       u32x4 y;
       if (!recv(y)) return;
+      load_part(b, own);
       const u32x4 res = R::op(R::pre(own), y);
       const uint32_t bn = b == 0 ? n - 1 : b - 1;   // block of step s + 1
-      if (s + 1 < n) own = load(bn);
+      own = load(bn, s + 1 < n);   // the next step's own input (none after the last)
       if (s == n - 1) store(b, res);
       if (!send(res)) return;
       b = bn;
@@ -283,8 +297,8 @@ __global__ __launch_bounds__(1024) void ll_tree(const StepArgs a, const TreeTask
       return left >= (uint64_t)unit ? kVecBytes : (int)(left * ESZ);
     };
     auto load = [&](int q) -> u32x4 {
-      const int nb = nbytes_of(q);
-      return nb ? ld_any(a.send[r], pos_of(q) * ESZ, nb) : u32x4{0, 0, 0, 0};
+      const char* const cell = static_cast<const char*>(a.send[r]) + (first_cell + (uint64_t)q) * slice_elems * ESZ;
+      return ld_lane(cell, p * kVecBytes, nbytes_of(q));
     };
     auto store = [&](int q, const u32x4& x) {
       if (q > 0 && q + 1 < nslices) {   // inside the task: every lane holds a whole vector

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kXThreads) void xring(const StepArgs a, const XArgs
   const uint32_t t = threadIdx.x;
   const uint32_t prev = (r + n - 1) % n;
   const uint32_t f_out = c * n + r, f_in = c * n + prev;     // FIFO written / read
-  const uint32_t me = orders[(size_t)x.chan_ring[c] * kMaxRanks + r];
+  const uint32_t me = __builtin_amdgcn_readfirstlane(orders[(size_t)x.chan_ring[c] * kMaxRanks + r]);
   uint32_t* const head_out = x.head + (size_t)f_out * kXCounterStride;
   uint32_t* const head_in = x.head + (size_t)f_in * kXCounterStride;
   uint32_t* const tail_out = x.tail + (size_t)f_out * kXCounterStride;
@@ -257,10 +257,25 @@ __global__ __launch_bounds__(kXThreads) void xring(const StepArgs a, const XArgs
           if (pos[j] >= d.offset && pos[j] < end)
             nb[j] = end - pos[j] >= (uint64_t)unit ? kVecBytes : (int)((end - pos[j]) * ESZ);
         }
+        // The own input: whole vectors are loaded before the item is
+        // received (the loads overlap the wait; out-of-range offsets, no
+        // branch), a partial vector, only ever at a block's end, once it is
+        // in (own_part).  Loading both under conditions before the wait made
+        // the merge of the two a register copy that waited for every load.
+        const char* const own_cell =
+            static_cast<const char*>(a.send[me]) + ((uint64_t)d.first_cell + q) * kSliceElems * ESZ;
+        const auto own_rs = buffer_view(own_cell);
+        auto lane_off = [&](int j) { return ((uint32_t)j * kXThreads + t) * (uint32_t)kVecBytes; };
         auto own = [&](Vecs& v) {
 #pragma unroll
-          for (int j = 0; j < V; ++j)
-            v[j] = R::pre(nb[j] ? ld_any(a.send[me], pos[j] * ESZ, nb[j]) : u32x4{0, 0, 0, 0});
+          for (int j = 0; j < V; ++j) v[j] = ld_buf(own_rs, nb[j] == kVecBytes ? lane_off(j) : kNoLoad);
+        };
+        auto own_part = [&](Vecs& v) {
+#pragma unroll
+          for (int j = 0; j < V; ++j) {
+            if (nb[j] > 0 && nb[j] < kVecBytes) v[j] = ld_part(own_cell, lane_off(j), nb[j]);
+            v[j] = R::pre(v[j]);
+          }
         };
         auto out = [&](const Vecs& v) {
 #pragma unroll
@@ -270,11 +285,13 @@ __global__ __launch_bounds__(kXThreads) void xring(const StepArgs a, const XArgs
         Vecs v, y;
         if (s == 0) {
           own(v);
+          own_part(v);
           if (n == 1) out(v);   // one rank: its own block is the result
           else if (!send(v)) return;
         } else if (s < n) {
           own(v);
           if (!recv(y)) return;
+          own_part(v);
 #pragma unroll
           for (int j = 0; j < V; ++j) v[j] = R::op(v[j], y[j]);
           ack();

@@ -69,6 +69,13 @@ long env_long(const char* name, long fallback) {
 }
 
 // As env_long, but 0 is a valid value.
+// Smallest k with 2^k >= x (x >= 1).
+int ceil_log2(uint64_t x) {
+  int k = 0;
+  while (((uint64_t)1 << k) < x) ++k;
+  return k;
+}
+
 long env_count(const char* name, long fallback) {
   if (!debug_env()) return fallback;
   const char* v = std::getenv(name);
@@ -139,6 +146,7 @@ struct Plan {
   int group = 0, block = 0, grid = 0;
   size_t lds = 0;
   uint32_t height = 0;
+  bool dynamic = false;       // tree: short pieces, one workgroup each
   bool ll = false;            // runs the LL-protocol kernels (one workgroup)
   // stepwise ring across workgroups: xchan = [nch][2] loop ranges then [nch]
   // ring rows; xslices = slices per step, per loop
@@ -371,32 +379,59 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     p->keep(kTable, loops);
     p->keep(kOrders, orders);
   } else {
-    // One pipeline per resident workgroup (tasks per CU = occupancy, or the
-    // tuning override EMU_TREE_TASKS_PER_CU).
     const int occ_t = p->ll ? ll_occupancy(false, t, op, p->block, p->lds)
                             : stepwise_occupancy(false, t, op, p->block, p->lds, p->group);
-    const long per_cu = env_long("EMU_TREE_TASKS_PER_CU", occ_t);
     uint32_t h = 0;
     for (const auto& ch : c.topo.channels) h = std::max<uint32_t>(h, (uint32_t)ch.height);
-    // Pieces of at least min_piece * H slices, as long as the message still
-    // gives every CU a piece.  A piece pays 2H stages of fill and drain, and
-    // one piece per resident workgroup leaves a small message's pieces a
-    // slice or two each, so nearly every stage is fill or drain while eight
-    // waves per SIMD contend to issue each stage's scalar-heavy control.
-    // Measured on MI355X (slot protocol, one rank per wave; 2 alternating
-    // rounds): pieces of at least H slices ran 8 ranks x 1 / 2 / 4 MiB in
-    // 11.6 / 16.3 / 20.9 us instead of 17.7 / 19.8 / 22.0 (16 ranks x 1 MiB:
-    // 12.3 against 19.0 us) and left 8 MiB and up unchanged; 2H and longer
-    // were slower, as was any minimum with two ranks per wave (17-32 ranks)
-    // or below one slice per CU.  Debug knob EMU_TREE_PIECE_MIN.
-    const long min_piece = env_count("EMU_TREE_PIECE_MIN", !p->ll && p->group == 64 ? 1 : 0);
     const uint64_t cells = (count + slice_elems - 1) / slice_elems;
-    const uint64_t min_cells =
-        min_piece > 0 ? std::min<uint64_t>((uint64_t)min_piece * std::max<uint32_t>(h, 1), (cells + cus - 1) / cus)
-                      : 1;
     std::vector<TreeTask> tasks;
     std::vector<TreeNode> nodes;
-    build_tree_tasks(c.topo, count, unit, slice_elems, (uint64_t)cus * per_cu, &tasks, &nodes, min_cells);
+    // One rank per wave, slot protocol, and a message of at least one full
+    // round of resident workgroups at that length: short pieces of
+    // max(8, 2^ceil(log2 H)) slices, one workgroup each, which the hardware
+    // dispatches as slots free up.  Workgroups sharing a CU do not progress
+    // evenly (the older ones are served first), so with one long piece per
+    // resident workgroup the last quarter of the call ran with a CU's slots
+    // emptying one by one (kernel timestamps: same-length pieces ending
+    // between 98 and 205 us at 8 ranks x 64 MiB).  Short pieces keep every
+    // slot busy to the end; their fill and drain overlap the steady stages
+    // of the other workgroups.  Measured on MI355X against one piece per
+    // resident workgroup (2 alternating rounds, 8 ranks f32 and 15/16 ranks
+    // bf16): pieces of 8 slices 8-12% faster from 64 MiB per rank up at 8
+    // ranks, 2% at 32, equal at 16, 6-7% on 15 and 16 ranks x 32 MiB; 4
+    // slices 4-10% slower, 16 and 32 slices in between, lengths off a power
+    // of two slower still.  The number of pieces is capped (128 per CU), so
+    // the task table stays small; beyond that pieces grow.
+    const uint64_t short_piece = std::max<uint64_t>(8, (uint64_t)1 << ceil_log2(std::max<uint32_t>(h, 1)));
+    const uint64_t resident = (uint64_t)cus * (uint64_t)occ_t;
+    p->dynamic = !p->ll && p->group == 64 && env_long("EMU_TREE_LONG_PIECES", 0) == 0 &&
+                 cells >= short_piece * resident;
+    if (p->dynamic) {
+      const uint64_t cap = (uint64_t)cus * 128;
+      const uint64_t piece = std::max<uint64_t>(short_piece, (cells + cap - 1) / cap);
+      build_tree_tasks(c.topo, count, unit, slice_elems, cells, &tasks, &nodes, piece);
+    } else {
+      // One pipeline per resident workgroup (tasks per CU = occupancy, or
+      // the tuning override EMU_TREE_TASKS_PER_CU).
+      const long per_cu = env_long("EMU_TREE_TASKS_PER_CU", occ_t);
+      // Pieces of at least min_piece * H slices, as long as the message
+      // still gives every CU a piece.  A piece pays 2H stages of fill and
+      // drain, and one piece per resident workgroup leaves a small message's
+      // pieces a slice or two each, so nearly every stage is fill or drain
+      // while eight waves per SIMD contend to issue each stage's scalar-heavy
+      // control.  Measured on MI355X (slot protocol, one rank per wave; 2
+      // alternating rounds): pieces of at least H slices ran 8 ranks x 1 / 2
+      // / 4 MiB in 11.6 / 16.3 / 20.9 us instead of 17.7 / 19.8 / 22.0 (16
+      // ranks x 1 MiB: 12.3 against 19.0 us) and left 8 MiB and up unchanged;
+      // 2H and longer were slower, as was any minimum with two ranks per wave
+      // (17-32 ranks) or below one slice per CU.  Debug knob
+      // EMU_TREE_PIECE_MIN.
+      const long min_piece = env_count("EMU_TREE_PIECE_MIN", !p->ll && p->group == 64 ? 1 : 0);
+      const uint64_t min_cells =
+          min_piece > 0 ? std::min<uint64_t>((uint64_t)min_piece * std::max<uint32_t>(h, 1), (cells + cus - 1) / cus)
+                        : 1;
+      build_tree_tasks(c.topo, count, unit, slice_elems, (uint64_t)cus * per_cu, &tasks, &nodes, min_cells);
+    }
     p->ntasks = (uint32_t)tasks.size();
     p->height = h;
     p->keep(kTasks, tasks);
@@ -404,7 +439,9 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
   }
   const int occ = p->ll ? ll_occupancy(ring, t, op, p->block, p->lds)
                         : stepwise_occupancy(ring, t, op, p->block, p->lds, p->group);
-  p->grid = (int)std::max<uint64_t>(1, std::min<uint64_t>(p->ntasks, (uint64_t)cus * occ));
+  // Short tree pieces: one workgroup per piece (the hardware balances the
+  // CUs); otherwise at most the resident workgroups, each looping over tasks.
+  p->grid = (int)std::max<uint64_t>(1, p->dynamic ? p->ntasks : std::min<uint64_t>(p->ntasks, (uint64_t)cus * occ));
   return EMU_SUCCESS;
 }
 

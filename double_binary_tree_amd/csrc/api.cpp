@@ -465,9 +465,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.566156, 662830}, {0.447388, 715101}}, {{0.190283, 666783}, {0.164693, 825644}}},   // 8 ranks
-    {{{0.58276, 463972}, {0.818678, 405914}}, {{0.122294, 421278}, {0.630355, 463680}}},    // 16 ranks
-    {{{0.630444, 233494}, {0.705665, 177011}}, {{0.0689347, 196989}, {0.389274, 218333}}},  // 32 ranks
+    {{{0.567248, 662510}, {0.449372, 740910}}, {{0.191599, 666327}, {0.165258, 826482}}},   // 8 ranks
+    {{{0.583954, 464512}, {0.818161, 407236}}, {{0.12268, 421716}, {0.630191, 460904}}},    // 16 ranks
+    {{{0.63137, 233407}, {0.705061, 176828}}, {{0.068851, 197303}, {0.390255, 218429}}},    // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

@@ -442,6 +442,18 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
   // Short tree pieces: one workgroup per piece (the hardware balances the
   // CUs); otherwise at most the resident workgroups, each looping over tasks.
   p->grid = (int)std::max<uint64_t>(1, p->dynamic ? p->ntasks : std::min<uint64_t>(p->ntasks, (uint64_t)cus * occ));
+  // Stepwise ring with at least 12 tasks per resident workgroup: one
+  // workgroup per task.  Workgroups sharing a CU progress unevenly and a
+  // long task list per workgroup lets the gap grow (kernel timestamps, 8
+  // ranks x 256 MiB: workgroups of 32 tasks each ending between 680 and
+  // 836 us); one task each lets the hardware balance the CUs, at the cost
+  // of a workgroup start per task.  Measured on MI355X (2 alternating
+  // rounds): 8 ranks x 96 / 128 / 256 MiB 2 / 5 / 6% faster, 16 ranks bf16
+  // x 128 MiB 6%, 32 ranks f16 x 64 MiB 3%; at 8 tasks per workgroup
+  // (8 ranks x 64 MiB) 1% slower, so shorter lists keep the loop (as do the
+  // standalone reduce-scatter and all-gather, not measured so).
+  if (ring && coll == kAllReduce && !p->ll && p->ntasks >= 12 * (uint64_t)p->grid && p->ntasks <= 0x7fffffffu)
+    p->grid = (int)p->ntasks;
   return EMU_SUCCESS;
 }
 

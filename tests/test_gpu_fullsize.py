@@ -60,3 +60,23 @@ def test_mid_size_tree_pieces_every_element(name, count):
     w = replace(I.WORKLOADS[name], count=count)
     for algo in ("tree", "ring"):
         check_every_element(w, algo, inplace_modes=(False,))
+
+
+@pytest.mark.parametrize("name,count,algo,nch", [
+    ("chain8_f32", (3 << 21) + 37, "tree", None),
+    ("dtree16_bf16", (5 << 21) + 11, "tree", None),
+    ("dtree15_bf16", (5 << 21) + 5, "tree", None),
+    ("chain8_f32", (28 << 20) + 4099, "ring", 1),
+])
+def test_balanced_plans_ragged_every_element(name, count, algo, nch):
+    """Sizes with a ragged tail large enough for the plans that let the
+    hardware balance the CUs: the stepwise tree in short pieces of 8
+    slices, one workgroup each (at least one full round of resident
+    workgroups), and the stepwise ring with one workgroup per task (at
+    least 12 tasks per resident workgroup: 8 ranks x 112 MiB on one
+    channel).  Fused and stepwise, every element against the oracle."""
+    from dataclasses import replace
+    w = replace(I.WORKLOADS[name], count=count)
+    if nch is not None:
+        w = replace(w, nchannels=nch)
+    check_every_element(w, algo, inplace_modes=(False,))

@@ -127,7 +127,8 @@ extern "C" {
 
 /* Environment.  The library reads no environment variable unless EMU_DEBUG
  * is set.  With EMU_DEBUG set, tuning knobs (EMU_FUSED_BLOCKS_PER_CU,
- * EMU_FUSED_XCD_RUNS, EMU_TREE_TASKS_PER_CU, EMU_STEP_GROUP, EMU_XWG_SLOTS)
+ * EMU_FUSED_XCD_RUNS, EMU_TREE_TASKS_PER_CU, EMU_TREE_PIECE_MIN,
+ * EMU_TREE_LONG_PIECES, EMU_STEP_GROUP, EMU_XWG_SLOTS)
  * and test hooks that shorten the bounded waits (EMU_LL_SPIN_LIMIT,
  * EMU_XWG_SPIN_LIMIT) override the built-in values of plans built after
  * they are set; EMU_DEBUG=1 also prints every tree record at init.  They

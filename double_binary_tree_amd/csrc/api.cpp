@@ -477,9 +477,9 @@ struct Cost { double alpha_us, bw; };
 // (sweep_points.txt); `costfit profiles/sweep_points.txt --defaults`
 // prints this table.
 Cost g_cost[kCostClasses][2][2] = {   // [class][stepwise, fused][ring, tree]: {alpha us, bytes/us}
-    {{{0.567248, 662510}, {0.449372, 740910}}, {{0.191599, 666327}, {0.165258, 826482}}},   // 8 ranks
-    {{{0.583954, 464512}, {0.818161, 407236}}, {{0.12268, 421716}, {0.630191, 460904}}},    // 16 ranks
-    {{{0.63137, 233407}, {0.705061, 176828}}, {{0.068851, 197303}, {0.390255, 218429}}},    // 32 ranks
+    {{{0.567544, 671660}, {0.449822, 741354}}, {{0.191954, 668336}, {0.165805, 824927}}},   // 8 ranks
+    {{{0.583629, 463726}, {0.815003, 407189}}, {{0.122226, 422618}, {0.63201, 462468}}},    // 16 ranks
+    {{{0.630384, 233903}, {0.705246, 177256}}, {{0.0688502, 197104}, {0.388422, 218334}}},  // 32 ranks
 };
 
 double predict_us(const Comm& c, bool fused, Algo algo, double nbytes) {

@@ -62,21 +62,21 @@ def test_mid_size_tree_pieces_every_element(name, count):
         check_every_element(w, algo, inplace_modes=(False,))
 
 
-@pytest.mark.parametrize("name,count,algo,nch", [
-    ("chain8_f32", (3 << 21) + 37, "tree", None),
-    ("dtree16_bf16", (5 << 21) + 11, "tree", None),
-    ("dtree15_bf16", (5 << 21) + 5, "tree", None),
-    ("chain8_f32", (28 << 20) + 4099, "ring", 1),
+@pytest.mark.parametrize("name,count,algo,over", [
+    ("chain8_f32", (3 << 21) + 37, "tree", {}),
+    ("dtree16_bf16", (5 << 21) + 11, "tree", {}),
+    ("dtree15_bf16", (5 << 21) + 5, "tree", {}),
+    ("chain8_f32", (9 << 18) + 3, "tree", {"nranks": 16}),
+    ("chain8_f32", (28 << 20) + 4099, "ring", {"nchannels": 1}),
 ])
-def test_balanced_plans_ragged_every_element(name, count, algo, nch):
+def test_balanced_plans_ragged_every_element(name, count, algo, over):
     """Sizes with a ragged tail large enough for the plans that let the
-    hardware balance the CUs: the stepwise tree in short pieces of 8
-    slices, one workgroup each (at least one full round of resident
-    workgroups), and the stepwise ring with one workgroup per task (at
-    least 12 tasks per resident workgroup: 8 ranks x 112 MiB on one
-    channel).  Fused and stepwise, every element against the oracle."""
+    hardware balance the CUs: the stepwise tree in short pieces, one
+    workgroup each (at least one full round of resident workgroups; pieces
+    of 8 slices, and of 16 on a 16-rank single-node chain, depth 15), and
+    the stepwise ring with one workgroup per task (at least 12 tasks per
+    resident workgroup: 8 ranks x 112 MiB on one channel).  Fused and
+    stepwise, every element against the oracle."""
     from dataclasses import replace
-    w = replace(I.WORKLOADS[name], count=count)
-    if nch is not None:
-        w = replace(w, nchannels=nch)
+    w = replace(I.WORKLOADS[name], count=count, **over)
     check_every_element(w, algo, inplace_modes=(False,))

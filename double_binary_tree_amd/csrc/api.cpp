@@ -69,13 +69,6 @@ long env_long(const char* name, long fallback) {
 }
 
 // As env_long, but 0 is a valid value.
-// Smallest k with 2^k >= x (x >= 1).
-int ceil_log2(uint64_t x) {
-  int k = 0;
-  while (((uint64_t)1 << k) < x) ++k;
-  return k;
-}
-
 long env_count(const char* name, long fallback) {
   if (!debug_env()) return fallback;
   const char* v = std::getenv(name);
@@ -83,6 +76,13 @@ long env_count(const char* name, long fallback) {
   char* end = nullptr;
   const long x = std::strtol(v, &end, 10);
   return (end && *end == '\0' && x >= 0) ? x : fallback;
+}
+
+// Smallest k with 2^k >= x (x >= 1).
+int ceil_log2(uint64_t x) {
+  int k = 0;
+  while (((uint64_t)1 << k) < x) ++k;
+  return k;
 }
 
 // Every device allocation of the library goes through these two, which
@@ -401,14 +401,14 @@ int make_plan(Comm& c, Coll coll, Algo algo, int dev, uint64_t count, DType t, O
     // ranks, 2% at 32, equal at 16, 6-7% on 15 and 16 ranks x 32 MiB; 4
     // slices 4-10% slower, 16 and 32 slices in between, lengths off a power
     // of two slower still.  The number of pieces is capped (128 per CU), so
-    // the task table stays small; beyond that pieces grow.
+    // the task table stays small; beyond that pieces grow, in powers of two.
     const uint64_t short_piece = std::max<uint64_t>(8, (uint64_t)1 << ceil_log2(std::max<uint32_t>(h, 1)));
     const uint64_t resident = (uint64_t)cus * (uint64_t)occ_t;
     p->dynamic = !p->ll && p->group == 64 && env_long("EMU_TREE_LONG_PIECES", 0) == 0 &&
                  cells >= short_piece * resident;
     if (p->dynamic) {
       const uint64_t cap = (uint64_t)cus * 128;
-      const uint64_t piece = std::max<uint64_t>(short_piece, (cells + cap - 1) / cap);
+      const uint64_t piece = (uint64_t)1 << ceil_log2(std::max<uint64_t>(short_piece, (cells + cap - 1) / cap));
       build_tree_tasks(c.topo, count, unit, slice_elems, cells, &tasks, &nodes, piece);
     } else {
       // One pipeline per resident workgroup (tasks per CU = occupancy, or

@@ -26,6 +26,11 @@ CASES = [
     ("hier4x8_f16", "tree", "stepwise", 1 << 19, 20003),
     ("hier4x8_i64", "tree", "fused", 1 << 19, 20003),
     ("hier4x8_f32max", "ring", "stepwise", 1 << 19, 20003),
+    # the balanced plans: the stepwise tree in short pieces (24 MiB per rank),
+    # the stepwise ring with one workgroup per task (112 MiB per rank), each
+    # followed by a smaller call on the other plan
+    ("chain8_f32", "tree", "stepwise", (3 << 21) + 37, 1 << 20),
+    ("chain8_f32", "ring", "stepwise", (28 << 20) + 5, 1 << 20),
 ]
 
 
